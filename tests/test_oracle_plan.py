@@ -1,0 +1,135 @@
+"""Pins for the oracle's dispatch plan (counts, offsets, slots) and dispatch copy.
+
+Pinned by hand-worked examples (tests/golden/plan_examples.json), by the invariants
+the EFA article's buffer design implies (counts sum to T*k; each sender's rows are
+one contiguous chunk; a destination never receives more than N*T*max(R, E/N)
+rows), and by an independent brute force (sorting the pairs) on small inputs.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import moe_synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.mark.parametrize("case", json.load(open(os.path.join(GOLDEN, "plan_examples.json")))["cases"],
+                         ids=lambda c: c["name"])
+def test_plan_golden(case):
+    p = oracle.plan(np.array(case["idx"]), case["E"], case["n_src"], case["n_dst"], case["cap"])
+    for key in ("counts", "expert_off", "chunk_off", "pair_slot", "row_pair"):
+        assert p[key].tolist() == case[key], key
+
+
+def _random_idx(rng, T, E, k):
+    return np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+
+
+def _brute_force_expert_major(idx, E):
+    """Sort the (expert, token) keys of all pairs: row = position in the sorted list."""
+    T, k = idx.shape
+    keys = sorted((int(idx[t, j]), t, j) for t in range(T) for j in range(k))
+    slot = np.zeros((T, k), dtype=np.int64)
+    for row, (_, t, j) in enumerate(keys):
+        slot[t, j] = row
+    return slot
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (7, 3, 2), (50, 8, 2), (129, 16, 5), (300, 64, 6)])
+def test_plan_expert_major_brute_force(T, E, k):
+    rng = np.random.default_rng(T * 100 + E)
+    idx = _random_idx(rng, T, E, k)
+    p = oracle.plan(idx, E)
+    assert np.array_equal(p["pair_slot"], _brute_force_expert_major(idx, E))
+    counts = np.bincount(idx.ravel(), minlength=E)
+    assert np.array_equal(p["counts"][0], counts)
+    assert p["expert_off"][-1] == T * k and np.all(np.diff(p["expert_off"]) == counts)
+    assert np.array_equal(np.sort(p["pair_slot"].ravel()), np.arange(T * k))
+    assert np.array_equal(p["row_pair"][p["pair_slot"].ravel()], np.arange(T * k))
+
+
+def _check_ep_invariants(p, idx, E, n_src, n_dst, cap):
+    T, k = idx.shape
+    Ts, epr = T // n_src, E // n_dst
+    counts = p["counts"]
+    assert counts.sum() == T * k
+    for s in range(n_src):
+        assert np.array_equal(counts[s], np.bincount(idx[s * Ts:(s + 1) * Ts].ravel(), minlength=E))
+    # tight receive bound: a token sends at most min(k, E/N) rows to one destination
+    tight = n_src * Ts * min(k, epr)
+    slots = p["pair_slot"]
+    rows_used = p["row_pair"] >= 0
+    assert rows_used.sum() == T * k
+    assert len(np.unique(slots)) == T * k
+    for r in range(n_dst):
+        live = p["chunk_off"][r, n_src]
+        assert live <= tight <= cap
+        region = rows_used[r * cap:(r + 1) * cap]
+        assert region[:live].all() and not region[live:].any()   # packed, no gaps
+    for t in range(T):
+        s = t // Ts
+        for j in range(k):
+            e = int(idx[t, j])
+            r = e // epr
+            row = int(slots[t, j]) - r * cap
+            lo, hi = p["chunk_off"][r, s], p["chunk_off"][r, s + 1]
+            assert lo <= row < hi                       # inside sender s's one chunk
+    # inside a chunk: expert-major, then ascending token
+    for r in range(n_dst):
+        for s in range(n_src):
+            lo, hi = p["chunk_off"][r, s], p["chunk_off"][r, s + 1]
+            keys = []
+            for row in range(r * cap + lo, r * cap + hi):
+                pr = int(p["row_pair"][row])
+                keys.append((int(idx[pr // k, pr % k]), pr // k))
+            assert keys == sorted(keys)
+
+
+@pytest.mark.parametrize("n_src,n_dst,Ts,E,k", [(2, 2, 3, 4, 2), (4, 2, 16, 8, 3), (8, 4, 10, 32, 8),
+                                                (3, 3, 5, 9, 1)])
+def test_plan_ep_layout_invariants(n_src, n_dst, Ts, E, k):
+    rng = np.random.default_rng(n_src * 7 + E)
+    T = n_src * Ts
+    idx = _random_idx(rng, T, E, k)
+    cap = n_src * Ts * max(k, E // n_dst)
+    p = oracle.plan(idx, E, n_src, n_dst, cap)
+    _check_ep_invariants(p, idx, E, n_src, n_dst, cap)
+    # the global expert offsets do not depend on the layout
+    assert np.array_equal(p["expert_off"], oracle.plan(idx, E)["expert_off"])
+
+
+def test_plan_ep_zipf_workload_invariants():
+    wl = moe_synth.WORKLOADS["ep32_zipf"]
+    idx, w = moe_synth.zipf_routing(wl)
+    idx = idx.numpy()
+    p = oracle.plan(idx, wl.E, wl.n_src, wl.n_dst, wl.cap_rows_per_dst)
+    assert wl.cap_rows_per_dst == 49152
+    _check_ep_invariants(p, idx, wl.E, wl.n_src, wl.n_dst, wl.cap_rows_per_dst)
+    # Zipf: the destination holding the most popular experts receives the most rows
+    live = p["chunk_off"][:, -1]
+    assert live[0] == live.max() and live[0] > 4 * live.mean()
+
+
+def test_plan_rejects_bad_indices():
+    with pytest.raises(AssertionError):
+        oracle.plan(np.array([[0, 4]]), 4)
+    with pytest.raises(AssertionError):
+        oracle.plan(np.array([[1, 1]]), 4)
+
+
+def test_dispatch_copies_rows_bitwise():
+    rng = np.random.default_rng(9)
+    T, E, k, d = 40, 6, 3, 24
+    idx = _random_idx(rng, T, E, k)
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    p = oracle.plan(idx, E)
+    xd = oracle.dispatch(x, p["pair_slot"], T * k)
+    for t in range(T):
+        for j in range(k):
+            assert np.array_equal(xd[p["pair_slot"][t, j]].view(np.uint32), x[t].view(np.uint32))
+    # every row is filled by exactly the token row_pair names
+    assert np.array_equal(xd, x[p["row_pair"] // k])
