@@ -1,0 +1,215 @@
+/*
+ * libmoe — the Mixture-of-Experts layer's hot path on one AMD Instinct MI355X
+ * (gfx950): router with top-k gating, dispatch into expert-contiguous (or
+ * per-destination-rank contiguous) buffers, grouped SwiGLU GEMM, combine, and the
+ * backward of each step.
+ *
+ * [EFA] = Perplexity (N. Licker, K. Hu, V. Zaytsev, L. Chen), "Enabling
+ * trillion-parameter models on AWS EFA", 2025-11-04. Section names follow its table
+ * of contents. The article describes the layer only in prose; the readings this
+ * library takes where it is silent are stated at each call.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Memory: every pointer argument is DEVICE memory owned by the caller (allocate
+ *   it with hipMalloc or any device allocator). The library allocates nothing and
+ *   keeps no mutable global state; scratch space comes in through `ws`.
+ * - Layout: all matrices are row-major and dense. A "row" of a token tensor is
+ *   d contiguous elements. Rows and pointers must be 16-byte aligned
+ *   (d * element size % 16 == 0, pointers % 16 == 0); otherwise MOE_ERR_ALIGN.
+ * - dtype: MOE_BF16 (bfloat16 storage, float32 arithmetic, round-to-nearest-even
+ *   on every store) or MOE_F32. Gate weights, logits and weight gradients are
+ *   always float32; indices always int32.
+ * - Execution: each call only enqueues work on `stream` (a hipStream_t; NULL is
+ *   the default stream) and returns. Results are ready when the stream is. Calls
+ *   on one stream run in order, which also orders the reuse of buffers between
+ *   dispatch and combine ([EFA] Dispatch and combine: receive buffers are read
+ *   before later kernels overwrite them).
+ * - Errors: a non-zero moe_status_t means nothing was enqueued. All argument
+ *   checks run on the host before any HIP call. Problems only the device can see
+ *   (an expert id out of range, a token listing an expert twice, a destination
+ *   region over capacity) never cause out-of-bounds accesses: the offending pair is
+ *   skipped and a flag is raised in the dispatch workspace; read it with
+ *   moe_dispatch_status(). MOE_ERR_HIP reports a failed launch.
+ * - Determinism: no floating-point atomics anywhere; every output is bitwise
+ *   reproducible for the same inputs and sizes.
+ */
+#ifndef LIBMOE_MOE_H
+#define LIBMOE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef int32_t moe_status_t;
+#define MOE_OK               0
+#define MOE_ERR_INVALID_ARG  1  /* null pointer, negative size, bad flag or dtype  */
+#define MOE_ERR_SHAPE        2  /* sizes inconsistent (k > E, T % n_src, ...)       */
+#define MOE_ERR_ALIGN        3  /* row length or pointer not 16-byte aligned        */
+#define MOE_ERR_CAPACITY     4  /* workspace or destination region too small        */
+#define MOE_ERR_BAD_INDEX    5  /* (device flag) expert id out of range / repeated  */
+#define MOE_ERR_HIP          6  /* a HIP launch or query failed                     */
+#define MOE_ERR_UNSUPPORTED  7  /* sizes outside what the kernels implement         */
+
+typedef int32_t moe_dtype_t;
+#define MOE_F32   0
+#define MOE_BF16  1
+
+/* moe_route flags */
+#define MOE_ROUTE_RENORM        0  /* gates = softmax over the k selected logits     */
+#define MOE_ROUTE_FULL_SOFTMAX  1  /* gates = full softmax's probabilities of the k  */
+
+/* Where dispatched rows go. n_src = n_dst = 1 with cap_rows_per_dst = T*k is the
+ * plain expert-major layout. Otherwise the T tokens are n_src equal consecutive
+ * groups (source ranks) and the E experts n_dst equal consecutive groups
+ * (destination ranks; expert e lives on rank e / (E / n_dst)); destination r owns
+ * rows [r*cap, (r+1)*cap) of the dispatch buffer. */
+typedef struct moe_layout {
+    int32_t n_src;
+    int32_t n_dst;
+    int64_t cap_rows_per_dst;
+} moe_layout_t;
+
+int32_t     moe_abi_version(void);
+const char *moe_status_str(moe_status_t status);
+
+/* ------------------------------------------------------------------ router
+ * [EFA] Introduction: a small linear routing layer decides which experts multiply a
+ * token; [EFA] Send and receive buffers: each token goes to R (here k) of E experts.
+ *
+ *   logit[t,e] = sum_{i<d} x[t,i] * w_router[e,i]        (no bias)
+ *   computed in float32 as acc = fmaf(x[t,i], w[e,i], acc) for i = 0..d-1 from +0,
+ *   one fixed order, so the integer routing decision is reproducible exactly.
+ *   topk_idx[t,:] = the k largest logits, descending; equal logits -> lower id first.
+ *   topk_w[t,j]   = exp(l_j - l_0) / sum_{j'<k} exp(l_j' - l_0)   (MOE_ROUTE_RENORM)
+ *                 = full softmax probability of expert idx[t,j]    (MOE_ROUTE_FULL_SOFTMAX)
+ *   The gating function is not on the pages; softmax over the selection is the
+ *   reading that makes the gate-weighted average of combine a true average.
+ *
+ * x [T,d] dtype, w_router [E,d] dtype; logits [T,E] f32 (NULL: not written);
+ * topk_idx [T,k] int32; topk_w [T,k] f32. Limits: 1 <= k <= min(E, 32), E <= 512.
+ * T = 0 is a no-op. */
+moe_status_t moe_route(const void *x, const void *w_router, int64_t T, int64_t d, int32_t E,
+                       int32_t k, moe_dtype_t dtype, int32_t flags, float *logits,
+                       int32_t *topk_idx, float *topk_w, void *stream);
+
+/* ---------------------------------------------------------------- dispatch
+ * [EFA] Dispatch and combine: count the tokens of every expert (the article does it
+ * with atomics in shared memory of one block), take the cumulative sum of the
+ * counts as offsets that pack the tokens into contiguous per-destination send
+ * buffers, then copy the tokens in. [EFA] Send and receive buffers: each sender's
+ * rows at a destination are one contiguous chunk, so one write per peer suffices,
+ * and a destination receives at most N*T*max(R, E/N) rows.
+ *
+ * Plan (all int32 outputs):
+ *   counts     [n_src, E]        pairs of source s routed to expert e
+ *   expert_off [E+1]             exclusive cumulative sum of per-expert totals
+ *   chunk_off  [n_dst, n_src+1]  start of source s's chunk inside destination r;
+ *                                chunk_off[r][n_src] = rows live at r
+ *   pair_slot  [T, k]            row of pair (t, j) in x_disp
+ *   row_pair   [n_dst * cap]     t*k + j of the pair in each row; -1 where unused
+ * Row of pair (t,j) with s = t / (T/n_src), e = topk_idx[t,j], r = e / (E/n_dst):
+ *   r*cap + chunk_off[r][s] + sum_{e' in r, e' < e} counts[s][e']
+ *         + #{t' < t in source s routed to e}
+ * i.e. chunks by sender, experts ascending inside a chunk, tokens ascending inside
+ * an expert (a stable order: the article's atomics leave it open). With the
+ * expert-major layout this is expert_off[e] + #{t' < t routed to e}.
+ * Copy: x_disp[pair_slot[t,j], :] = x[t, :] (bit copy). Rows of x_disp that no pair
+ * uses are not written. x and x_disp may both be NULL (plan only).
+ *
+ * layout NULL = expert-major. Requires T % n_src == 0, E % n_dst == 0 and
+ * cap_rows_per_dst >= (T/n_src) * n_src * min(k, E/n_dst) (the tight form of the
+ * article's bound: a token sends at most min(k, E/N) rows to one destination).
+ * Tokens must list k distinct experts in [0, E); violations raise the device flag.
+ * ws: at least moe_dispatch_workspace_size() bytes, 256-byte aligned; its first
+ * bytes hold the device status flag that moe_dispatch_status() reads. */
+size_t moe_dispatch_workspace_size(int64_t T, int32_t E, int32_t k, const moe_layout_t *layout);
+moe_status_t moe_dispatch(const void *x, const int32_t *topk_idx, int64_t T, int64_t d,
+                          int32_t E, int32_t k, moe_dtype_t dtype, const moe_layout_t *layout,
+                          int32_t *counts, int32_t *expert_off, int32_t *chunk_off,
+                          int32_t *pair_slot, int32_t *row_pair, void *x_disp, void *ws,
+                          size_t ws_bytes, void *stream);
+/* Waits for `stream`, then returns MOE_OK, MOE_ERR_BAD_INDEX or MOE_ERR_CAPACITY
+ * from the flag the last moe_dispatch on `ws` raised. */
+moe_status_t moe_dispatch_status(const void *ws, void *stream);
+
+/* -------------------------------------------------------------- expert FFN
+ * [EFA] MoE all-to-all over EFA: grouped GEMM kernels multiply the received tokens
+ * with the expert weights; [EFA] Dispatch and combine: the receiver moves tokens
+ * into the tensor handed to the grouped GEMM. Expert form (not on the pages):
+ * SwiGLU without biases. For every expert e, rows R_e = [expert_off[e],
+ * expert_off[e+1]) of the expert-major x_disp:
+ *   h = X W1^T, u = X W3^T, a = silu(h) * u with silu(z) = z / (1 + exp(-z)),
+ *   y_disp[R_e] = a W2^T
+ * w13 [E, 2F, d] (rows 0..F-1 = W1, F..2F-1 = W3), w2 [E, d, F], x_disp and y_disp
+ * [rows, d], rows >= expert_off[E] (the host cannot see expert_off: rows is the
+ * allocation). float32 accumulation; bf16 stores round to nearest even (a is
+ * stored in bf16 between the two GEMMs). hu_save [rows, 2F] (NULL: not written)
+ * keeps h and u for the backward. Requires d % 64 == 0 and F % 64 == 0 for bf16.
+ * ws: moe_expert_ffn_workspace_size() bytes. */
+size_t moe_expert_ffn_workspace_size(int32_t E, int64_t rows, int64_t d, int64_t F,
+                                     moe_dtype_t dtype);
+moe_status_t moe_expert_ffn(const void *x_disp, const int32_t *expert_off, const void *w13,
+                            const void *w2, int32_t E, int64_t rows, int64_t d, int64_t F,
+                            moe_dtype_t dtype, void *y_disp, void *hu_save, void *ws,
+                            size_t ws_bytes, void *stream);
+
+/* ----------------------------------------------------------------- combine
+ * [EFA] Introduction and Dispatch and combine: the combine kernel returns each
+ * token's processed copies and computes their weighted average into the output
+ * tensor, accumulating at the receiver ([EFA] Dispatch/combine latency).
+ *   y[t,:] = sum_{j<k} topk_w[t,j] * y_disp[pair_slot[t,j], :]
+ * float32 accumulation in j order, one rounding to dtype. rows_total bounds
+ * pair_slot (entries outside [0, rows_total) contribute nothing). */
+moe_status_t moe_combine(const void *y_disp, const int32_t *pair_slot, const float *topk_w,
+                         int64_t T, int32_t k, int64_t d, int64_t rows_total, moe_dtype_t dtype,
+                         void *y, void *stream);
+
+/* ---------------------------------------------------------------- backward
+ * The transposes of the steps above (the layer's gradient; the article covers
+ * only the forward data movement).
+ *
+ * moe_combine_bwd:  dy_disp[pair_slot[t,j]] = topk_w[t,j] * dy[t]      (dtype)
+ *                   dtopk_w[t,j] = <dy[t], y_disp[pair_slot[t,j]]>    (f32)
+ * moe_expert_ffn_bwd, per expert e with X, dO = dy_disp rows of e, h, u from hu_save:
+ *                   dA = dO W2;  dh = dA * u * s * (1 + h (1 - s)), s = sigmoid(h);
+ *                   du = dA * silu(h);  dX = dh W1 + du W3      -> dx_disp (dtype)
+ *                   dW2 = dO^T a;  dW1 = dh^T X;  dW3 = du^T X  -> dw2, dw13 (f32)
+ * moe_route_bwd:    dlogits_sel[t,j] = g_j (dg_j - sum_i g_i dg_i)   (f32, RENORM)
+ *                   dw_router[e,:] = sum over pairs (t,j) with idx e of
+ *                                    dlogits_sel[t,j] * x[t,:]        (f32)
+ * moe_dispatch_bwd: dx[t] = sum_j dx_disp[pair_slot[t,j]]
+ *                           + sum_j dlogits_sel[t,j] * w_router[topk_idx[t,j]]
+ *                   (second term skipped if dlogits_sel is NULL), float32 sum in
+ *                   j order, one rounding to dtype.
+ * Shapes as in the forward calls; dw13 [E,2F,d], dw2 [E,d,F], dw_router [E,d]. */
+moe_status_t moe_combine_bwd(const void *dy, const void *y_disp, const int32_t *pair_slot,
+                             const float *topk_w, int64_t T, int32_t k, int64_t d,
+                             int64_t rows_total, moe_dtype_t dtype, void *dy_disp,
+                             float *dtopk_w, void *stream);
+size_t moe_expert_ffn_bwd_workspace_size(int32_t E, int64_t rows, int64_t d, int64_t F,
+                                         moe_dtype_t dtype);
+moe_status_t moe_expert_ffn_bwd(const void *x_disp, const void *dy_disp, const void *hu_save,
+                                const int32_t *expert_off, const void *w13, const void *w2,
+                                int32_t E, int64_t rows, int64_t d, int64_t F,
+                                moe_dtype_t dtype, void *dx_disp, float *dw13, float *dw2,
+                                void *ws, size_t ws_bytes, void *stream);
+size_t moe_route_bwd_workspace_size(int64_t T, int64_t d, int32_t E, int32_t k);
+moe_status_t moe_route_bwd(const void *x, const int32_t *topk_idx, const float *topk_w,
+                           const float *dtopk_w, int64_t T, int64_t d, int32_t E, int32_t k,
+                           moe_dtype_t dtype, float *dlogits_sel, float *dw_router, void *ws,
+                           size_t ws_bytes, void *stream);
+moe_status_t moe_dispatch_bwd(const void *dx_disp, const int32_t *pair_slot,
+                              const int32_t *topk_idx, const float *dlogits_sel,
+                              const void *w_router, int64_t T, int32_t k, int64_t d, int32_t E,
+                              int64_t rows_total, moe_dtype_t dtype, void *dx, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBMOE_MOE_H */

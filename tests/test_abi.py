@@ -1,0 +1,107 @@
+"""The C ABI on the CPU: libmoe.so loads, exports every entry point include/moe.h
+declares, and rejects bad arguments on the host before any HIP call (so these run
+without a GPU: every call here returns before touching the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import token_routing_expert_router_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+OK, INVALID, SHAPE, ALIGN, CAPACITY, BAD_INDEX, HIP, UNSUPPORTED = range(8)
+F32, BF16 = 0, 1
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return moe.load()
+
+
+def test_library_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+    # the binding declares the same set
+    assert set(names) == set(moe.EXPORTED)
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.moe_abi_version() == 1
+    for s in range(8):
+        assert lib.moe_status_str(s)
+    assert lib.moe_status_str(99) == b"unknown status"
+
+
+FAKE = 1 << 20          # a 16-byte aligned non-null address never dereferenced
+
+
+def test_route_host_validation(lib):
+    r = lib.moe_route
+    assert r(FAKE, FAKE, 10, 64, 8, 9, BF16, 0, None, FAKE, FAKE, None) == SHAPE      # k > E
+    assert r(FAKE, FAKE, 10, 64, 8, 0, BF16, 0, None, FAKE, FAKE, None) == INVALID    # k = 0
+    assert r(FAKE, FAKE, 10, 64, 8, 2, 7, 0, None, FAKE, FAKE, None) == INVALID       # dtype
+    assert r(FAKE, FAKE, 10, 64, 8, 2, BF16, 5, None, FAKE, FAKE, None) == INVALID    # flags
+    assert r(FAKE, FAKE, 10, 60, 8, 2, BF16, 0, None, FAKE, FAKE, None) == ALIGN      # 120 B rows
+    assert r(FAKE + 8, FAKE, 10, 64, 8, 2, BF16, 0, None, FAKE, FAKE, None) == ALIGN
+    assert r(None, FAKE, 10, 64, 8, 2, BF16, 0, None, FAKE, FAKE, None) == INVALID
+    assert r(FAKE, FAKE, 10, 64, 600, 2, BF16, 0, None, FAKE, FAKE, None) == UNSUPPORTED
+    assert r(FAKE, FAKE, 10, 64, 64, 33, BF16, 0, None, FAKE, FAKE, None) == UNSUPPORTED
+    assert r(None, None, 0, 64, 8, 2, BF16, 0, None, None, None, None) == OK          # empty
+
+
+def _layout(n_src, n_dst, cap):
+    return ctypes.byref(moe._Layout(n_src, n_dst, cap))
+
+
+def test_dispatch_host_validation(lib):
+    d = lib.moe_dispatch
+    ws_sz = lib.moe_dispatch_workspace_size(4096, 384, 8, _layout(32, 32, 49152))
+    assert ws_sz > 0
+    args = lambda **kw: [kw.get("x", FAKE), FAKE, kw.get("T", 4096), kw.get("d", 7168),
+                         kw.get("E", 384), kw.get("k", 8), BF16, kw.get("lay", _layout(32, 32, 49152)),
+                         FAKE, FAKE, FAKE, FAKE, FAKE, kw.get("xd", FAKE), kw.get("ws", FAKE),
+                         kw.get("wsb", ws_sz), None]
+    # tight bound: 32 * 128 * min(8, 12) = 32768 rows per destination
+    assert d(*args(lay=_layout(32, 32, 32767))) == CAPACITY
+    assert d(*args(lay=_layout(32, 30, 49152))) == SHAPE         # 384 % 30
+    assert d(*args(lay=_layout(33, 32, 49152))) == SHAPE         # 4096 % 33
+    assert d(*args(lay=_layout(0, 32, 49152))) == INVALID
+    assert d(*args(wsb=ws_sz - 1)) == CAPACITY
+    assert d(*args(ws=FAKE + 16)) == ALIGN                        # 256-byte workspace
+    assert d(*args(x=None)) == INVALID                            # x and x_disp together
+    assert d(*args(k=400)) == SHAPE
+    assert d(*args(E=2048, lay=None, k=8, T=16)) == UNSUPPORTED
+
+
+def test_ffn_combine_bwd_host_validation(lib):
+    f = lib.moe_expert_ffn
+    need = lib.moe_expert_ffn_workspace_size(64, 24576, 2048, 1408, BF16)
+    assert need >= 24576 * 1408 * 2
+    base = [FAKE, FAKE, FAKE, FAKE, 64, 24576, 2048, 1408, BF16, FAKE, None, FAKE, need, None]
+    bad = list(base); bad[7] = 1400                                 # F % 64
+    assert f(*bad) == UNSUPPORTED
+    bad = list(base); bad[12] = need - 1
+    assert f(*bad) == CAPACITY
+    bad = list(base); bad[11] = FAKE + 16
+    assert f(*bad) == ALIGN
+    bad = list(base); bad[2] = None
+    assert f(*bad) == INVALID
+    c = lib.moe_combine
+    assert c(FAKE, FAKE, FAKE, 10, 2, 60, 20, BF16, FAKE, None) == ALIGN
+    assert c(FAKE, FAKE, FAKE, 10, 0, 64, 20, BF16, FAKE, None) == INVALID
+    assert c(None, None, None, 0, 2, 64, 0, BF16, None, None) == OK
+    cb = lib.moe_combine_bwd
+    assert cb(FAKE, FAKE, FAKE, FAKE, 10, 40, 64, 20, BF16, FAKE, FAKE, None) == UNSUPPORTED
+    db = lib.moe_dispatch_bwd
+    assert db(FAKE, FAKE, None, FAKE, None, 10, 2, 64, 8, 20, BF16, FAKE, None) == INVALID

@@ -1,0 +1,256 @@
+"""GPU parity of the forward path: libmoe (through its C ABI) against the CPU oracle.
+
+Bars: routing indices, counts, offsets, slots and dispatch buffers bit-exact; router
+logits bit-exact (same float32 order on both sides); float outputs within normwise
+relative error 2e-2 for bf16 and 1e-5 for float32 (max |got - ref| / max |ref|).
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 2e-2
+F32_TOL = 1e-5
+
+
+def _tol(wl):
+    return F32_TOL if wl.dtype == "f32" else BF16_TOL
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy() if t.is_floating_point() else t.cpu().numpy()
+
+
+def _wl(name, **kw):
+    return moe_synth.small_workload(moe_synth.WORKLOADS[name], **kw)
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+ROUTE_CASES = [
+    ("tiny_f32", {}),
+    ("mid_bf16", dict(T=1000)),                       # ragged: not a multiple of the tile
+    ("mid_bf16", dict(T=1)),
+    ("large_bf16", dict(T=333)),
+    ("mid_bf16", dict(T=257, d=136, E=5, k=5)),       # k = E, d not a multiple of 32
+    ("mid_bf16", dict(T=64, d=64, E=512, k=32)),      # largest E and k
+    ("mid_bf16", dict(T=40, d=64, E=1, k=1)),
+]
+
+
+@pytest.mark.parametrize("name,kw", ROUTE_CASES, ids=[f"{n}-{kw}" for n, kw in ROUTE_CASES])
+def test_route_parity(gpu_lib, name, kw):
+    moe = gpu_lib
+    wl = _wl(name, **kw)
+    _say(f"route {wl}")
+    inp = moe_synth.layer_inputs(wl, with_experts=False)
+    x, w = inp["x"].cuda(), inp["w_router"].cuda()
+    idx, gates, logits = moe.moe_route(x, w, wl.k, want_logits=True)
+    torch.cuda.synchronize()
+    ref_logits, ref_idx, ref_g = oracle.route(inp["x"], inp["w_router"], wl.k)
+    got = logits.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), ref_logits.view(np.uint32)), "logits differ"
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+    assert oracle.normwise_rel_err(_np(gates), ref_g) <= F32_TOL
+
+
+def test_route_full_softmax_flag(gpu_lib):
+    moe = gpu_lib
+    wl = _wl("mid_bf16", T=300, E=64, k=6)
+    inp = moe_synth.layer_inputs(wl, with_experts=False)
+    idx, gates, _ = moe.moe_route(inp["x"].cuda(), inp["w_router"].cuda(), wl.k, flags=1)
+    torch.cuda.synchronize()
+    ref_idx, ref_g = oracle.topk_gating(oracle.router_logits(inp["x"], inp["w_router"]), wl.k,
+                                        renorm=False)
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+    assert oracle.normwise_rel_err(_np(gates), ref_g) <= F32_TOL
+
+
+def _check_plan(out, ref, rows_live_only=True):
+    for key in ("counts", "expert_off", "chunk_off", "pair_slot"):
+        got = out[key].cpu().numpy().reshape(ref[key].shape)
+        assert np.array_equal(got, ref[key]), key
+    assert np.array_equal(out["row_pair"].cpu().numpy(), ref["row_pair"]), "row_pair"
+
+
+DISPATCH_CASES = [
+    ("tiny_f32", {}),
+    ("mid_bf16", dict(T=1000, d=256)),
+    ("mid_bf16", dict(T=3, d=64, E=8, k=3)),
+    ("large_bf16", dict(T=600, d=512)),
+]
+
+
+@pytest.mark.parametrize("name,kw", DISPATCH_CASES, ids=[f"{n}-{kw}" for n, kw in DISPATCH_CASES])
+def test_dispatch_parity_expert_major(gpu_lib, name, kw):
+    moe = gpu_lib
+    wl = _wl(name, **kw)
+    _say(f"dispatch {wl}")
+    inp = moe_synth.layer_inputs(wl, with_experts=False)
+    x = inp["x"].cuda()
+    idx, gates, _ = moe.moe_route(x, inp["w_router"].cuda(), wl.k)
+    out = moe.moe_dispatch(x, idx, wl.E)
+    assert moe.moe_dispatch_status(out["ws"]) == 0
+    _, ref_idx, ref_g = oracle.route(inp["x"], inp["w_router"], wl.k)
+    ref = oracle.plan(ref_idx, wl.E)
+    _check_plan(out, ref)
+    xd = out["x_disp"].cpu()
+    ref_xd = torch.from_numpy(oracle.dispatch(inp["x"], ref["pair_slot"], wl.pairs)).to(xd.dtype)
+    assert torch.equal(xd.view(torch.int16) if xd.dtype == torch.bfloat16 else xd.view(torch.int32),
+                       ref_xd.view(torch.int16) if xd.dtype == torch.bfloat16 else ref_xd.view(torch.int32))
+    # identity experts: combine(dispatch(x)) == x, bit-exact after one rounding
+    y = moe.moe_combine(out["x_disp"], out["pair_slot"], gates)
+    torch.cuda.synchronize()
+    if wl.dtype == "bf16":
+        assert torch.equal(y.cpu(), inp["x"])
+    else:
+        assert oracle.normwise_rel_err(_np(y), inp["x"].numpy()) <= F32_TOL
+
+
+def test_dispatch_ep_layout_zipf_full(gpu_lib):
+    """32 source ranks x 128 tokens, d=7168, E=384, R=8, Zipf(1.2), buffers sized to
+    N*T*max(R,E/N) = 49152 rows per destination."""
+    moe = gpu_lib
+    wl = moe_synth.WORKLOADS["ep32_zipf"]
+    _say(f"ep dispatch {wl}")
+    idx, w = moe_synth.zipf_routing(wl)
+    x = moe_synth.layer_inputs(wl, device="cuda", with_experts=False)["x"]
+    lay = moe.Layout(wl.n_src, wl.n_dst, wl.cap_rows_per_dst)
+    out = moe.moe_dispatch(x, idx.cuda(), wl.E, layout=lay)
+    assert moe.moe_dispatch_status(out["ws"]) == 0
+    ref = oracle.plan(idx.numpy(), wl.E, wl.n_src, wl.n_dst, wl.cap_rows_per_dst)
+    _check_plan(out, ref)
+    # the article's bound, and its tight form, per destination
+    live = out["chunk_off"][:, -1].cpu().numpy()
+    assert live.max() <= wl.n_src * wl.tokens_per_src * min(wl.k, wl.E // wl.n_dst)
+    assert live.max() <= wl.cap_rows_per_dst
+    # every live row holds its token bit-exactly
+    rp = out["row_pair"]
+    live_rows = torch.nonzero(rp >= 0).squeeze(1)
+    toks = (rp[live_rows] // wl.k).long()
+    assert torch.equal(out["x_disp"][live_rows].view(torch.int16), x[toks].view(torch.int16))
+    # identity experts, and random expert outputs against the oracle's combine
+    y = moe.moe_combine(out["x_disp"], out["pair_slot"], w.cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(y, x)
+    rows = wl.n_dst * wl.cap_rows_per_dst
+    y_disp = torch.zeros((rows, wl.d), dtype=torch.bfloat16, device="cuda")
+    y_disp[live_rows] = moe_synth.random_rows(wl, live_rows.numel(), device="cuda")
+    y2 = moe.moe_combine(y_disp, out["pair_slot"], w.cuda())
+    torch.cuda.synchronize()
+    sample = torch.arange(0, wl.T, 37)
+    ref_y = oracle.combine(y_disp.cpu(), ref["pair_slot"][sample.numpy()], w.numpy()[sample.numpy()])
+    assert oracle.normwise_rel_err(_np(y2[sample.cuda()]), ref_y) <= BF16_TOL
+    del y_disp, out
+    torch.cuda.empty_cache()
+
+
+def test_dispatch_device_flags(gpu_lib):
+    moe = gpu_lib
+    idx = torch.tensor([[0, 1], [2, 8], [3, 3], [1, 2]], dtype=torch.int32, device="cuda")
+    x = torch.randn((4, 64), device="cuda").to(torch.bfloat16)
+    out = moe.moe_dispatch(x, idx, 8)
+    assert moe.moe_dispatch_status(out["ws"]) == 5             # MOE_ERR_BAD_INDEX
+    ps = out["pair_slot"].cpu().numpy()
+    assert ps[1, 1] == -1                                        # the out-of-range pair
+    ok = torch.tensor([[0, 1], [2, 7], [3, 4], [1, 2]], dtype=torch.int32, device="cuda")
+    out = moe.moe_dispatch(x, ok, 8, out={"ws": out["ws"]})     # the flag is overwritten
+    assert moe.moe_dispatch_status(out["ws"]) == 0
+    # experts that receive no token leave empty segments
+    assert out["counts"].cpu().numpy().tolist() == [[1, 2, 2, 1, 1, 0, 0, 1]]
+    assert out["expert_off"].cpu().numpy().tolist() == [0, 1, 3, 5, 6, 7, 7, 7, 8]
+
+
+FFN_CASES = [
+    ("tiny_f32", {}),
+    ("mid_bf16", dict(T=700)),
+    ("mid_bf16", dict(T=96, d=128, E=4, k=2, F=64)),
+    ("large_bf16", dict(T=96, d=7168, E=24, k=8, F=2048)),
+]
+
+
+@pytest.mark.parametrize("name,kw", FFN_CASES, ids=[f"{n}-{kw}" for n, kw in FFN_CASES])
+def test_layer_forward_parity(gpu_lib, name, kw):
+    moe = gpu_lib
+    wl = _wl(name, **kw)
+    _say(f"forward {wl}")
+    inp = moe_synth.layer_inputs(wl)
+    dev = {n: t.cuda() for n, t in inp.items()}
+    out = moe.forward(dev["x"], dev["w_router"], dev["w13"], dev["w2"], wl.k)
+    torch.cuda.synchronize()
+    ref = oracle.forward(inp["x"], inp["w_router"], inp["w13"], inp["w2"], wl.k)
+    assert np.array_equal(out["topk_idx"].cpu().numpy(), ref["idx"])
+    assert np.array_equal(out["pair_slot"].cpu().numpy(), ref["pair_slot"])
+    e_ffn = oracle.normwise_rel_err(_np(out["y_disp"]), ref["y_disp"])
+    e_y = oracle.normwise_rel_err(_np(out["y"]), ref["y"])
+    _say(f"  y_disp err {e_ffn:.3e}  y err {e_y:.3e}")
+    assert e_ffn <= _tol(wl) and e_y <= _tol(wl)
+
+
+def test_mid_bf16_full_forward(gpu_lib):
+    """The full T=4096, d=2048, E=64, k=6, F=1408 layer, in the configuration the
+    benchmark times, against the full oracle."""
+    moe = gpu_lib
+    wl = moe_synth.WORKLOADS["mid_bf16"]
+    _say(f"full forward {wl}")
+    inp = moe_synth.layer_inputs(wl, device="cuda")
+    out = moe.forward(inp["x"], inp["w_router"], inp["w13"], inp["w2"], wl.k)
+    torch.cuda.synchronize()
+    host = {n: t.cpu() for n, t in inp.items()}
+    ref = oracle.forward(host["x"], host["w_router"], host["w13"], host["w2"], wl.k)
+    assert np.array_equal(out["topk_idx"].cpu().numpy(), ref["idx"])
+    for key in ("counts", "expert_off", "pair_slot", "row_pair"):
+        assert np.array_equal(out[key].cpu().numpy().reshape(ref[key].shape), ref[key]), key
+    e_y = oracle.normwise_rel_err(_np(out["y"]), ref["y"])
+    e_ffn = oracle.normwise_rel_err(_np(out["y_disp"]), ref["y_disp"])
+    _say(f"  y_disp err {e_ffn:.3e}  y err {e_y:.3e}")
+    assert e_y <= BF16_TOL and e_ffn <= BF16_TOL
+    # bitwise determinism
+    out2 = moe.forward(inp["x"], inp["w_router"], inp["w13"], inp["w2"], wl.k)
+    torch.cuda.synchronize()
+    assert torch.equal(out["y"], out2["y"]) and torch.equal(out["y_disp"], out2["y_disp"])
+
+
+def test_large_bf16_full_forward_sampled(gpu_lib):
+    """T=8192, d=7168, E=384, k=8, F=2048 with all 34 GB of expert weights resident:
+    routing and plan checked for every token, outputs for a sample of tokens computed
+    one by one by the oracle."""
+    moe = gpu_lib
+    wl = moe_synth.WORKLOADS["large_bf16"]
+    _say(f"large forward {wl}")
+    inp = moe_synth.layer_inputs(wl, device="cuda")
+    out = moe.forward(inp["x"], inp["w_router"], inp["w13"], inp["w2"], wl.k)
+    torch.cuda.synchronize()
+    x_h, wr_h = inp["x"].cpu(), inp["w_router"].cpu()
+    _, ref_idx, ref_g = oracle.route(x_h, wr_h, wl.k)
+    assert np.array_equal(out["topk_idx"].cpu().numpy(), ref_idx)
+    ref = oracle.plan(ref_idx, wl.E)
+    for key in ("counts", "expert_off", "pair_slot", "row_pair"):
+        assert np.array_equal(out[key].cpu().numpy().reshape(ref[key].shape), ref[key]), key
+    sample = np.array([0, 1, 4095, 8191])
+    w13, w2 = inp["w13"], inp["w2"]
+    _, _, y_ref = oracle.forward_tokens(x_h[sample], wr_h, wl.k,
+                                        lambda e: (w13[e].cpu(), w2[e].cpu()))
+    err = oracle.normwise_rel_err(_np(out["y"][torch.from_numpy(sample).cuda()]), y_ref)
+    _say(f"  sampled y err {err:.3e}")
+    assert err <= BF16_TOL
+    del inp, out, w13, w2
+    torch.cuda.empty_cache()
+
+
+def test_empty_and_tiny_inputs(gpu_lib):
+    moe = gpu_lib
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    w = torch.randn((8, 64), device="cuda").to(torch.bfloat16)
+    idx, g, _ = moe.moe_route(x, w, 2)
+    assert idx.shape == (0, 2)
+    out = moe.moe_dispatch(x, idx, 8)
+    y = moe.moe_combine(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"), idx, g)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 64)

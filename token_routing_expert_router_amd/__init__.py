@@ -1,0 +1,297 @@
+"""Python binding of libmoe, the MI355X-native Mixture-of-Experts layer.
+
+Argument marshalling only: every step of the layer runs in libmoe's HIP kernels.
+Each function has the name of the C entry point it calls (declared in
+include/moe.h); tensors are torch tensors on the GPU, and the call is enqueued on
+torch's current stream. Outputs may be passed in; otherwise they are allocated
+with torch (device memory is the one thing PyTorch provides here).
+
+If libmoe.so is missing or fails to load, every call raises: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["MoEError", "load", "library_path", "moe_abi_version", "moe_route", "moe_dispatch",
+           "moe_dispatch_status", "moe_expert_ffn", "moe_combine", "moe_combine_bwd",
+           "moe_expert_ffn_bwd", "moe_route_bwd", "moe_dispatch_bwd", "Layout", "forward",
+           "EXPORTED"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libmoe.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+MOE_ROUTE_RENORM, MOE_ROUTE_FULL_SOFTMAX = 0, 1
+_STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN",
+           4: "MOE_ERR_CAPACITY", 5: "MOE_ERR_BAD_INDEX", 6: "MOE_ERR_HIP",
+           7: "MOE_ERR_UNSUPPORTED"}
+
+_P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+
+# entry point -> (restype, argtypes); the same list include/moe.h declares
+EXPORTED = {
+    "moe_abi_version": (_I32, []),
+    "moe_status_str": (ctypes.c_char_p, [_I32]),
+    "moe_route": (_I32, [_P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P]),
+    "moe_dispatch_workspace_size": (_SZ, [_I64, _I32, _I32, _P]),
+    "moe_dispatch": (_I32, [_P, _P, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
+                            _P, _SZ, _P]),
+    "moe_dispatch_status": (_I32, [_P, _P]),
+    "moe_expert_ffn_workspace_size": (_SZ, [_I32, _I64, _I64, _I64, _I32]),
+    "moe_expert_ffn": (_I32, [_P, _P, _P, _P, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _SZ,
+                              _P]),
+    "moe_combine": (_I32, [_P, _P, _P, _I64, _I32, _I64, _I64, _I32, _P, _P]),
+    "moe_combine_bwd": (_I32, [_P, _P, _P, _P, _I64, _I32, _I64, _I64, _I32, _P, _P, _P]),
+    "moe_expert_ffn_bwd_workspace_size": (_SZ, [_I32, _I64, _I64, _I64, _I32]),
+    "moe_expert_ffn_bwd": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I32, _P, _P,
+                                  _P, _P, _SZ, _P]),
+    "moe_route_bwd_workspace_size": (_SZ, [_I64, _I64, _I32, _I32]),
+    "moe_route_bwd": (_I32, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _SZ, _P]),
+    "moe_dispatch_bwd": (_I32, [_P, _P, _P, _P, _P, _I64, _I32, _I64, _I32, _I64, _I32, _P,
+                                _P]),
+}
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {_STATUS.get(status, status)}")
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [("n_src", ctypes.c_int32), ("n_dst", ctypes.c_int32),
+                ("cap_rows_per_dst", ctypes.c_int64)]
+
+
+class Layout:
+    """Where dispatched rows go (see moe_layout_t). None means expert-major."""
+
+    def __init__(self, n_src: int, n_dst: int, cap_rows_per_dst: int):
+        self.n_src, self.n_dst, self.cap = int(n_src), int(n_dst), int(cap_rows_per_dst)
+
+    def _c(self):
+        return _Layout(self.n_src, self.n_dst, self.cap)
+
+
+_lib = None
+
+
+def load():
+    """Load libmoe.so (once). Raises if it is missing: there is no fallback."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(f"libmoe.so not found at {library_path}; build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        lib = ctypes.CDLL(library_path)
+        for name, (res, args) in EXPORTED.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise MoEError(fn, status)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    assert t.is_cuda and t.is_contiguous(), "tensors must be contiguous GPU tensors"
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def moe_abi_version() -> int:
+    return int(load().moe_abi_version())
+
+
+# ------------------------------------------------------------------ forward
+def moe_route(x, w_router, k: int, *, flags: int = MOE_ROUTE_RENORM, logits=None,
+              want_logits: bool = False, topk_idx=None, topk_w=None, stream=None):
+    """Router logits, top-k selection and gates. Returns (topk_idx, topk_w, logits)."""
+    T, d = x.shape
+    E = w_router.shape[0]
+    dev = x.device
+    if want_logits and logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _check("moe_route", load().moe_route(_ptr(x), _ptr(w_router), T, d, E, k, _dt(x), flags,
+                                         _ptr(logits), _ptr(topk_idx), _ptr(topk_w),
+                                         _stream(stream)))
+    return topk_idx, topk_w, logits
+
+
+def moe_dispatch(x, topk_idx, E: int, *, layout: Optional[Layout] = None, d: Optional[int] = None,
+                 dtype: Optional[torch.dtype] = None, out: Optional[dict] = None, stream=None):
+    """Plan (+ copy unless x is None). Returns a dict with counts, expert_off,
+    chunk_off, pair_slot, row_pair, x_disp (None if x is None) and ws."""
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    if x is not None:
+        d = x.shape[1]
+        dtype = x.dtype
+    n_src = layout.n_src if layout else 1
+    n_dst = layout.n_dst if layout else 1
+    cap = layout.cap if layout else T * k
+    lib = load()
+    clay = layout._c() if layout else None
+    lay_ptr = ctypes.byref(clay) if clay is not None else None
+    o = dict(out or {})
+    ws_bytes = int(lib.moe_dispatch_workspace_size(T, E, k, lay_ptr))
+    if o.get("ws") is None:
+        o["ws"] = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    for name, shape in (("counts", (n_src, E)), ("expert_off", (E + 1,)),
+                        ("chunk_off", (n_dst, n_src + 1)), ("pair_slot", (T, k)),
+                        ("row_pair", (n_dst * cap,))):
+        if o.get(name) is None:
+            o[name] = torch.empty(shape, dtype=torch.int32, device=dev)
+    if x is not None and o.get("x_disp") is None:
+        o["x_disp"] = torch.empty((n_dst * cap, d), dtype=dtype, device=dev)
+    if x is None:
+        o["x_disp"] = None
+    dt = _dt(x) if x is not None else (MOE_BF16 if dtype in (None, torch.bfloat16) else MOE_F32)
+    _check("moe_dispatch", lib.moe_dispatch(
+        _ptr(x), _ptr(topk_idx), T, d if d is not None else 8, E, k, dt, lay_ptr,
+        _ptr(o["counts"]), _ptr(o["expert_off"]), _ptr(o["chunk_off"]), _ptr(o["pair_slot"]),
+        _ptr(o["row_pair"]), _ptr(o["x_disp"]), _ptr(o["ws"]), o["ws"].numel(), _stream(stream)))
+    return o
+
+
+def moe_dispatch_status(ws, stream=None) -> int:
+    """Synchronises, then returns the device flag of the last dispatch on ws."""
+    return int(load().moe_dispatch_status(_ptr(ws), _stream(stream)))
+
+
+def moe_expert_ffn(x_disp, expert_off, w13, w2, *, y_disp=None, hu_save=None, ws=None,
+                   stream=None):
+    rows, d = x_disp.shape
+    E, F2, _ = w13.shape
+    F = F2 // 2
+    lib = load()
+    need = int(lib.moe_expert_ffn_workspace_size(E, rows, d, F, _dt(x_disp)))
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x_disp.device)
+    if y_disp is None:
+        y_disp = torch.empty((rows, d), dtype=x_disp.dtype, device=x_disp.device)
+    _check("moe_expert_ffn", lib.moe_expert_ffn(
+        _ptr(x_disp), _ptr(expert_off), _ptr(w13), _ptr(w2), E, rows, d, F, _dt(x_disp),
+        _ptr(y_disp), _ptr(hu_save), _ptr(ws), ws.numel(), _stream(stream)))
+    return y_disp
+
+
+def moe_combine(y_disp, pair_slot, topk_w, *, y=None, stream=None):
+    T, k = pair_slot.shape
+    rows, d = y_disp.shape
+    if y is None:
+        y = torch.empty((T, d), dtype=y_disp.dtype, device=y_disp.device)
+    _check("moe_combine", load().moe_combine(_ptr(y_disp), _ptr(pair_slot), _ptr(topk_w), T, k,
+                                             d, rows, _dt(y_disp), _ptr(y), _stream(stream)))
+    return y
+
+
+# ----------------------------------------------------------------- backward
+def moe_combine_bwd(dy, y_disp, pair_slot, topk_w, *, dy_disp=None, dtopk_w=None, stream=None):
+    T, k = pair_slot.shape
+    rows, d = y_disp.shape
+    if dy_disp is None:
+        dy_disp = torch.empty((rows, d), dtype=dy.dtype, device=dy.device)
+    if dtopk_w is None:
+        dtopk_w = torch.empty((T, k), dtype=torch.float32, device=dy.device)
+    _check("moe_combine_bwd", load().moe_combine_bwd(
+        _ptr(dy), _ptr(y_disp), _ptr(pair_slot), _ptr(topk_w), T, k, d, rows, _dt(dy),
+        _ptr(dy_disp), _ptr(dtopk_w), _stream(stream)))
+    return dy_disp, dtopk_w
+
+
+def moe_expert_ffn_bwd(x_disp, dy_disp, hu_save, expert_off, w13, w2, *, dx_disp=None,
+                       dw13=None, dw2=None, ws=None, stream=None):
+    rows, d = x_disp.shape
+    E, F2, _ = w13.shape
+    F = F2 // 2
+    dev = x_disp.device
+    lib = load()
+    need = int(lib.moe_expert_ffn_bwd_workspace_size(E, rows, d, F, _dt(x_disp)))
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if dx_disp is None:
+        dx_disp = torch.empty((rows, d), dtype=x_disp.dtype, device=dev)
+    if dw13 is None:
+        dw13 = torch.empty((E, 2 * F, d), dtype=torch.float32, device=dev)
+    if dw2 is None:
+        dw2 = torch.empty((E, d, F), dtype=torch.float32, device=dev)
+    _check("moe_expert_ffn_bwd", lib.moe_expert_ffn_bwd(
+        _ptr(x_disp), _ptr(dy_disp), _ptr(hu_save), _ptr(expert_off), _ptr(w13), _ptr(w2), E,
+        rows, d, F, _dt(x_disp), _ptr(dx_disp), _ptr(dw13), _ptr(dw2), _ptr(ws), ws.numel(),
+        _stream(stream)))
+    return dx_disp, dw13, dw2
+
+
+def moe_route_bwd(x, topk_idx, topk_w, dtopk_w, E: int, *, dlogits_sel=None, dw_router=None,
+                  ws=None, stream=None):
+    T, d = x.shape
+    k = topk_idx.shape[1]
+    lib = load()
+    need = int(lib.moe_route_bwd_workspace_size(T, d, E, k))
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    if dlogits_sel is None:
+        dlogits_sel = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    if dw_router is None:
+        dw_router = torch.empty((E, d), dtype=torch.float32, device=x.device)
+    _check("moe_route_bwd", lib.moe_route_bwd(
+        _ptr(x), _ptr(topk_idx), _ptr(topk_w), _ptr(dtopk_w), T, d, E, k, _dt(x),
+        _ptr(dlogits_sel), _ptr(dw_router), _ptr(ws), ws.numel(), _stream(stream)))
+    return dlogits_sel, dw_router
+
+
+def moe_dispatch_bwd(dx_disp, pair_slot, *, topk_idx=None, dlogits_sel=None, w_router=None,
+                     dx=None, stream=None):
+    T, k = pair_slot.shape
+    rows, d = dx_disp.shape
+    E = w_router.shape[0] if w_router is not None else 0
+    if dx is None:
+        dx = torch.empty((T, d), dtype=dx_disp.dtype, device=dx_disp.device)
+    _check("moe_dispatch_bwd", load().moe_dispatch_bwd(
+        _ptr(dx_disp), _ptr(pair_slot), _ptr(topk_idx), _ptr(dlogits_sel), _ptr(w_router), T, k,
+        d, E, rows, _dt(dx_disp), _ptr(dx), _stream(stream)))
+    return dx
+
+
+# ------------------------------------------------------------ whole layer
+def forward(x, w_router, w13, w2, k: int, *, save_for_backward: bool = False, stream=None):
+    """route -> dispatch -> expert FFN -> combine. Returns a dict of all outputs."""
+    E = w_router.shape[0]
+    F = w13.shape[1] // 2
+    idx, gates, _ = moe_route(x, w_router, k, stream=stream)
+    plan = moe_dispatch(x, idx, E, stream=stream)
+    hu = None
+    if save_for_backward:
+        hu = torch.empty((plan["x_disp"].shape[0], 2 * F), dtype=x.dtype, device=x.device)
+    y_disp = moe_expert_ffn(plan["x_disp"], plan["expert_off"], w13, w2, hu_save=hu,
+                            stream=stream)
+    y = moe_combine(y_disp, plan["pair_slot"], gates, stream=stream)
+    return dict(topk_idx=idx, topk_w=gates, y_disp=y_disp, y=y, hu_save=hu, **plan)

@@ -1,0 +1,143 @@
+// Combine: each token's expert outputs come back and are averaged with the gate
+// weights, y[t] = sum_j w[t,j] * y_disp[pair_slot[t,j]]. [EFA] = Perplexity,
+// "Enabling trillion-parameter models on AWS EFA" (2025): the combine kernel is the
+// dual of dispatch and computes the weighted average of the returned tokens
+// (Introduction); it reuses the routing information dispatch produced and
+// accumulates from the receive buffers into the output tensor (Dispatch and combine);
+// accumulation happens at the receiver only (Dispatch/combine latency).
+//
+// One wavefront per token; lane c owns 16-byte column chunks c, c+64, ...; the k
+// gathered rows are independent 16-byte loads (kept in flight together), summed in
+// float32 in j order and rounded once. The backward is the transpose: a scatter of
+// w*dy into the k rows, and a dot product per (t, j) for the gate gradient.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_combine(const uint4 *__restrict__ y_disp,
+                                                 const int *__restrict__ pair_slot,
+                                                 const float *__restrict__ topk_w, int T, int k,
+                                                 int rc, int64_t rows_total,
+                                                 uint4 *__restrict__ y) {
+    constexpr int VN = Vec<DT>::N;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave0 = __builtin_amdgcn_readfirstlane((blockIdx.x * blockDim.x + threadIdx.x) / kWave);
+    const int nwaves = gridDim.x * blockDim.x / kWave;
+    for (int t = wave0; t < T; t += nwaves) {
+        const int *ps = pair_slot + size_t(t) * k;
+        const float *pw = topk_w + size_t(t) * k;
+        for (int c = lane; c < rc; c += kWave) {
+            float acc[VN];
+#pragma unroll
+            for (int i = 0; i < VN; ++i) acc[i] = 0.0f;
+            for (int j = 0; j < k; ++j) {
+                const int s = ps[j];
+                if (s < 0 || s >= rows_total) continue;
+                const float g = pw[j];
+                float f[VN];
+                Vec<DT>::unpack(y_disp[size_t(s) * rc + c], f);
+#pragma unroll
+                for (int i = 0; i < VN; ++i) acc[i] = __builtin_fmaf(g, f[i], acc[i]);
+            }
+            y[size_t(t) * rc + c] = Vec<DT>::pack(acc);
+        }
+    }
+}
+
+// dy_disp[pair_slot[t,j]] = w[t,j] * dy[t];  dtopk_w[t,j] = <dy[t], y_disp[pair_slot[t,j]]>
+// (one pass over the row per j; the token's dy row stays in cache between passes)
+template <int DT>
+__global__ __launch_bounds__(256) void k_combine_bwd(const uint4 *__restrict__ dy,
+                                                     const uint4 *__restrict__ y_disp,
+                                                     const int *__restrict__ pair_slot,
+                                                     const float *__restrict__ topk_w, int T,
+                                                     int k, int rc, int64_t rows_total,
+                                                     uint4 *__restrict__ dy_disp,
+                                                     float *__restrict__ dtopk_w) {
+    constexpr int VN = Vec<DT>::N;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave0 = __builtin_amdgcn_readfirstlane((blockIdx.x * blockDim.x + threadIdx.x) / kWave);
+    const int nwaves = gridDim.x * blockDim.x / kWave;
+    for (int t = wave0; t < T; t += nwaves) {
+        for (int j = 0; j < k; ++j) {
+            const int s = pair_slot[size_t(t) * k + j];
+            const bool ok = s >= 0 && s < rows_total;
+            const float w = topk_w[size_t(t) * k + j];
+            float dot = 0.0f;
+            if (ok) {
+                for (int c = lane; c < rc; c += kWave) {
+                    float g[VN], f[VN], o[VN];
+                    Vec<DT>::unpack(dy[size_t(t) * rc + c], g);
+                    Vec<DT>::unpack(y_disp[size_t(s) * rc + c], f);
+#pragma unroll
+                    for (int i = 0; i < VN; ++i) {
+                        dot = __builtin_fmaf(g[i], f[i], dot);
+                        o[i] = w * g[i];
+                    }
+                    dy_disp[size_t(s) * rc + c] = Vec<DT>::pack(o);
+                }
+            }
+#pragma unroll
+            for (int off = kWave / 2; off > 0; off >>= 1) dot += __shfl_xor(dot, off, kWave);
+            if (lane == 0) dtopk_w[size_t(t) * k + j] = dot;
+        }
+    }
+}
+
+int row_grid(int64_t T) { return int(std::min<int64_t>(cdiv(T, 4), 8192)); }
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" moe_status_t moe_combine(const void *y_disp, const int32_t *pair_slot,
+                                    const float *topk_w, int64_t T, int32_t k, int64_t d,
+                                    int64_t rows_total, moe_dtype_t dtype, void *y, void *stream) {
+    if (!valid_dtype(dtype) || T < 0 || d <= 0 || k <= 0 || rows_total < 0)
+        return MOE_ERR_INVALID_ARG;
+    if (T > (int64_t(1) << 31) / 64) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!y_disp || !pair_slot || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+    const int64_t rowb = d * elt_size(dtype);
+    if (rowb % 16 != 0 || !aligned16(y_disp) || !aligned16(y)) return MOE_ERR_ALIGN;
+    const hipStream_t st = as_stream(stream);
+    if (dtype == MOE_BF16)
+        hipLaunchKernelGGL(k_combine<MOE_BF16>, dim3(row_grid(T)), dim3(256), 0, st,
+                           static_cast<const uint4 *>(y_disp), pair_slot, topk_w, int(T), k,
+                           int(rowb / 16), rows_total, static_cast<uint4 *>(y));
+    else
+        hipLaunchKernelGGL(k_combine<MOE_F32>, dim3(row_grid(T)), dim3(256), 0, st,
+                           static_cast<const uint4 *>(y_disp), pair_slot, topk_w, int(T), k,
+                           int(rowb / 16), rows_total, static_cast<uint4 *>(y));
+    return launch_status();
+}
+
+extern "C" moe_status_t moe_combine_bwd(const void *dy, const void *y_disp,
+                                        const int32_t *pair_slot, const float *topk_w, int64_t T,
+                                        int32_t k, int64_t d, int64_t rows_total,
+                                        moe_dtype_t dtype, void *dy_disp, float *dtopk_w,
+                                        void *stream) {
+    if (!valid_dtype(dtype) || T < 0 || d <= 0 || k <= 0 || rows_total < 0)
+        return MOE_ERR_INVALID_ARG;
+    if (k > 32 || T > (int64_t(1) << 31) / 64) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!dy || !y_disp || !pair_slot || !topk_w || !dy_disp || !dtopk_w) return MOE_ERR_INVALID_ARG;
+    const int64_t rowb = d * elt_size(dtype);
+    if (rowb % 16 != 0 || !aligned16(dy) || !aligned16(y_disp) || !aligned16(dy_disp))
+        return MOE_ERR_ALIGN;
+    const hipStream_t st = as_stream(stream);
+    if (dtype == MOE_BF16)
+        hipLaunchKernelGGL(k_combine_bwd<MOE_BF16>, dim3(row_grid(T)), dim3(256), 0, st,
+                           static_cast<const uint4 *>(dy), static_cast<const uint4 *>(y_disp),
+                           pair_slot, topk_w, int(T), k, int(rowb / 16), rows_total,
+                           static_cast<uint4 *>(dy_disp), dtopk_w);
+    else
+        hipLaunchKernelGGL(k_combine_bwd<MOE_F32>, dim3(row_grid(T)), dim3(256), 0, st,
+                           static_cast<const uint4 *>(dy), static_cast<const uint4 *>(y_disp),
+                           pair_slot, topk_w, int(T), k, int(rowb / 16), rows_total,
+                           static_cast<uint4 *>(dy_disp), dtopk_w);
+    return launch_status();
+}

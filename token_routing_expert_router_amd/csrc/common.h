@@ -1,0 +1,67 @@
+// Internal helpers shared by the libmoe translation units (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;  // CDNA wavefront width
+
+// Device status flag bits (first int32 of the dispatch workspace).
+constexpr int kFlagBadIndex = 1;
+constexpr int kFlagCapacity = 2;
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline int64_t elt_size(moe_dtype_t dt) { return dt == MOE_BF16 ? 2 : 4; }
+inline bool valid_dtype(moe_dtype_t dt) { return dt == MOE_BF16 || dt == MOE_F32; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline moe_status_t launch_status() {
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// bf16 <-> f32. Widening is exact; narrowing is round-to-nearest-even
+// (gfx950 lowers the cast to v_cvt_pk_bf16_f32).
+__device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xffff0000u); }
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    __bf16 b = static_cast<__bf16>(f);
+    return __builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return uint32_t(f32_to_bf16_bits(lo)) | (uint32_t(f32_to_bf16_bits(hi)) << 16);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// 16 bytes of a row as 8 floats (bf16) or 4 floats (f32).
+template <int DT> struct Vec;
+template <> struct Vec<MOE_BF16> {
+    static constexpr int N = 8;
+    __device__ __forceinline__ static void unpack(const uint4 &v, float *f) {
+        f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+        f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+    }
+    __device__ __forceinline__ static uint4 pack(const float *f) {
+        return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                          pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+    }
+};
+template <> struct Vec<MOE_F32> {
+    static constexpr int N = 4;
+    __device__ __forceinline__ static void unpack(const uint4 &v, float *f) {
+        f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+        f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+    }
+    __device__ __forceinline__ static uint4 pack(const float *f) {
+        return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]),
+                          __float_as_uint(f[2]), __float_as_uint(f[3]));
+    }
+};
+
+}  // namespace moe

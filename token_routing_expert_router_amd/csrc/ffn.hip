@@ -1,0 +1,424 @@
+// Expert FFN: the grouped GEMM that multiplies each expert's rows by that expert's
+// SwiGLU weights. [EFA] = Perplexity, "Enabling trillion-parameter models on AWS EFA"
+// (2025): after dispatch, grouped GEMM kernels multiply the tokens with the expert
+// weights (MoE all-to-all over EFA); the receiver moves tokens into the tensor handed
+// to the grouped GEMM (Dispatch and combine). The expert form is not on the pages:
+// SwiGLU without biases, h = X W1^T, u = X W3^T, a = silu(h) * u, y = a W2^T.
+//
+// bf16 path (the only matrix-core path in the library): v_mfma_f32_32x32x16_bf16,
+// float32 accumulation. Workgroup tile 128 rows x 256 weight rows x 64 deep, four
+// wavefronts in a 2x2 grid, each 64 rows x 4 sub-tiles of 32 weight rows. For the
+// gate/up GEMM the 256 weight rows are 128 rows of W1 and the same 128 rows of W3,
+// so the SwiGLU epilogue pairs h and u in registers and only a is written. Tiles are
+// double-buffered in LDS with an XOR swizzle of 16-byte chunks. Rows are ragged per
+// expert: a tile map (m-tiles per expert, prefix-summed on the device) lets a
+// persistent grid walk (expert, m-tile, n-tile) work items; the walk gives each XCD
+// a contiguous run of items in every round so tiles that share A rows or weight
+// panels meet in the same L2.
+//
+// f32 path: a plain LDS-tiled vector-ALU kernel (float32 has no dense matrix-core
+// peak worth the complexity at the sizes it is used for).
+#include "common.h"
+
+#include <mutex>
+
+namespace moe {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 128;         // token rows per tile
+constexpr int BNW = 256;        // weight rows per tile
+constexpr int BK = 64;          // depth per LDS stage
+constexpr int kGemmThreads = 256;
+constexpr int kLdsA = BM * BK * 2;              // bytes per A stage
+constexpr int kLdsB = BNW * BK * 2;             // bytes per B stage
+constexpr int kLdsGemm = 2 * (kLdsA + kLdsB);   // double buffered
+
+enum { EPI_SWIGLU = 0, EPI_PLAIN = 1 };
+
+// 16-byte chunk c of LDS row r lives at chunk c ^ swz(r): 8 consecutive rows (and
+// the even/odd rows of 16 consecutive rows) land on distinct bank groups.
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+
+__device__ __forceinline__ float silu_f(float h) { return h / (1.0f + __expf(-h)); }
+
+// m-tiles per expert, prefix summed: tile_off[e] = sum_{e'<e} ceil(M_e'/tile_rows).
+__global__ void k_tile_map(const int *__restrict__ expert_off, int E, int tile_rows,
+                           int *__restrict__ tile_off) {
+    __shared__ int buf[1024];
+    const int tid = threadIdx.x;
+    int v = 0;
+    if (tid < E) v = (max(expert_off[tid + 1] - expert_off[tid], 0) + tile_rows - 1) / tile_rows;
+    const int own = v;
+    for (int off = 1; off < 1024; off <<= 1) {
+        buf[tid] = v;
+        __syncthreads();
+        if (tid >= off) v += buf[tid - off];
+        __syncthreads();
+    }
+    if (tid < E) tile_off[tid] = v - own;
+    if (tid == E - 1) tile_off[E] = v;
+}
+
+template <int EPI>
+__global__ __launch_bounds__(kGemmThreads) void k_gemm_bf16(
+    const uint16_t *__restrict__ A,        // [rows, K]
+    const int *__restrict__ expert_off,    // [E+1]
+    const int *__restrict__ tile_off,      // [E+1]
+    int E, const uint16_t *__restrict__ W, // [E, Nw, K]
+    int K, int N, int64_t rows_alloc,
+    uint16_t *__restrict__ out,            // [rows, N]
+    uint16_t *__restrict__ hu_save,        // [rows, 2N] (gate/up only; may be null)
+    int n_tiles) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int Nw = (EPI == EPI_SWIGLU) ? 2 * N : N;   // weight rows per expert
+    const int total = tile_off[E] * n_tiles;
+    const int G = gridDim.x;
+    // this workgroup's place in a round: XCD (blockIdx % 8) gets a contiguous run
+    const int per = G / 8;
+    const int slot = (G % 8 == 0) ? (blockIdx.x % 8) * per + blockIdx.x / 8 : blockIdx.x;
+
+    for (int base = 0; base < total; base += G) {
+        const int item = base + slot;
+        if (item >= total) break;
+        const int mt = item / n_tiles, nt = item % n_tiles;
+        // expert owning m-tile mt: largest e with tile_off[e] <= mt
+        int lo = 0, hi = E;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (tile_off[mid] <= mt) lo = mid; else hi = mid;
+        }
+        const int e = lo;
+        const int m0 = expert_off[e] + (mt - tile_off[e]) * BM;
+        // rows past the allocation are never written, whatever expert_off holds
+        const int m_end = int(min<int64_t>(expert_off[e + 1], rows_alloc));
+        const int n0 = nt * (EPI == EPI_SWIGLU ? BNW / 2 : BNW);
+        const uint16_t *We = W + size_t(e) * Nw * K;
+
+        // global source rows of this thread's chunks (clamped: out-of-range rows
+        // compute garbage that is never stored)
+        const uint16_t *a_src[4];
+        const uint16_t *b_src[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = tid + i * kGemmThreads;
+            int64_t r = int64_t(m0) + c / 8;
+            if (r >= rows_alloc) r = rows_alloc - 1;
+            if (r < 0) r = 0;
+            a_src[i] = A + r * K + (c % 8) * 8;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int c = tid + i * kGemmThreads;
+            const int br = c / 8;
+            int wr;
+            if (EPI == EPI_SWIGLU) {
+                const int n = min(n0 + (br & 127), N - 1);
+                wr = (br < 128) ? n : N + n;
+            } else {
+                wr = min(n0 + br, N - 1);
+            }
+            b_src[i] = We + size_t(wr) * K + (c % 8) * 8;
+        }
+        u32x4 ra[4], rb[8];
+#define MOE_GLOAD(k0)                                                                   \
+    do {                                                                                \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i)                                   \
+            ra[i] = *reinterpret_cast<const u32x4 *>(a_src[i] + (k0));                  \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i)                                   \
+            rb[i] = *reinterpret_cast<const u32x4 *>(b_src[i] + (k0));                  \
+    } while (0)
+#define MOE_LSTORE(buf)                                                                 \
+    do {                                                                                \
+        unsigned char *As_ = lds + (buf) * (kLdsA + kLdsB);                             \
+        unsigned char *Bs_ = As_ + kLdsA;                                               \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                 \
+            const int c = tid + i * kGemmThreads, r = c / 8, kc = c % 8;                \
+            *reinterpret_cast<u32x4 *>(As_ + r * 128 + ((kc ^ swz(r)) << 4)) = ra[i];   \
+        }                                                                               \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                 \
+            const int c = tid + i * kGemmThreads, r = c / 8, kc = c % 8;                \
+            *reinterpret_cast<u32x4 *>(Bs_ + r * 128 + ((kc ^ swz(r)) << 4)) = rb[i];   \
+        }                                                                               \
+    } while (0)
+
+        f32x16 acc[2][4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+        // B rows of this wave's four 32-row sub-tiles
+        int brow[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            brow[s] = (EPI == EPI_SWIGLU) ? (s >> 1) * 128 + wn * 64 + (s & 1) * 32
+                                          : wn * 128 + s * 32;
+
+        const int KT = K / BK;
+        __syncthreads();          // previous item's readers are done with LDS
+        MOE_GLOAD(0);
+        MOE_LSTORE(0);
+        __syncthreads();
+        for (int kt = 0; kt < KT; ++kt) {
+            const int cur = kt & 1;
+            if (kt + 1 < KT) MOE_GLOAD((kt + 1) * BK);
+            const unsigned char *As = lds + cur * (kLdsA + kLdsB);
+            const unsigned char *Bs = As + kLdsA;
+#pragma unroll
+            for (int ks = 0; ks < BK / 16; ++ks) {
+                const int kc = ks * 2 + (lane >> 5);
+                bf16x8 af[2], bfr[4];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int r = wm * 64 + i * 32 + (lane & 31);
+                    af[i] = *reinterpret_cast<const bf16x8 *>(As + r * 128 + ((kc ^ swz(r)) << 4));
+                }
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int r = brow[s] + (lane & 31);
+                    bfr[s] = *reinterpret_cast<const bf16x8 *>(Bs + r * 128 + ((kc ^ swz(r)) << 4));
+                }
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        acc[i][s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[s], acc[i][s], 0, 0, 0);
+            }
+            if (kt + 1 < KT) MOE_LSTORE(cur ^ 1);
+            __syncthreads();
+        }
+
+#undef MOE_GLOAD
+#undef MOE_LSTORE
+        // epilogue: lane holds column (lane & 31) of each 32x32 sub-tile and rows
+        // 8*(v/4) + 4*(lane/32) + v%4 for v = 0..15
+        const int col_l = lane & 31;
+        const int row_l = 4 * (lane >> 5);
+        if (EPI == EPI_SWIGLU) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const int col = n0 + wn * 64 + s2 * 32 + col_l;
+                    if (col >= N) continue;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + row_l + (v & 3);
+                        if (row < 0 || row >= m_end) continue;
+                        const float h = acc[i][s2][v], u = acc[i][s2 + 2][v];
+                        out[size_t(row) * N + col] = f32_to_bf16_bits(silu_f(h) * u);
+                        if (hu_save) {
+                            hu_save[size_t(row) * 2 * N + col] = f32_to_bf16_bits(h);
+                            hu_save[size_t(row) * 2 * N + N + col] = f32_to_bf16_bits(u);
+                        }
+                    }
+                }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int col = n0 + wn * 128 + s * 32 + col_l;
+                    if (col >= N) continue;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + row_l + (v & 3);
+                        if (row < 0 || row >= m_end) continue;
+                        out[size_t(row) * N + col] = f32_to_bf16_bits(acc[i][s][v]);
+                    }
+                }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- f32 path
+// 64x64 output tile per workgroup, 16-deep LDS stages, 4x4 outputs per thread.
+// Gate/up computes h and u tiles side by side (W1 rows and the matching W3 rows).
+constexpr int FT = 64, FK = 16;
+
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm_f32(const float *__restrict__ A,
+                                                  const int *__restrict__ expert_off,
+                                                  const int *__restrict__ tile_off, int E,
+                                                  const float *__restrict__ W, int K, int N,
+                                                  int64_t rows_alloc, float *__restrict__ out,
+                                                  float *__restrict__ hu_save, int n_tiles) {
+    constexpr int NB = (EPI == EPI_SWIGLU) ? 2 : 1;   // weight tiles (W1, W3)
+    __shared__ float As[FK][FT + 1];
+    __shared__ float Bs[NB][FK][FT + 1];
+    const int tid = threadIdx.x;
+    const int tr = tid / 16, tc = tid % 16;
+    const int Nw = NB * N;
+    const int total = tile_off[E] * n_tiles;
+    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+        const int mt = item / n_tiles, nt = item % n_tiles;
+        int lo = 0, hi = E;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (tile_off[mid] <= mt) lo = mid; else hi = mid;
+        }
+        const int e = lo;
+        const int m0 = expert_off[e] + (mt - tile_off[e]) * FT;
+        const int m_end = int(min<int64_t>(expert_off[e + 1], rows_alloc));
+        const int n0 = nt * FT;
+        const float *We = W + size_t(e) * Nw * K;
+        float acc[NB][4][4] = {};
+        for (int k0 = 0; k0 < K; k0 += FK) {
+            __syncthreads();
+            for (int c = tid; c < FT * FK; c += 256) {
+                const int r = c / FK, kk = c % FK;
+                const int row = m0 + r, kg = k0 + kk;
+                As[kk][r] = (row >= 0 && row < m_end && kg < K) ? A[size_t(row) * K + kg] : 0.0f;
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const int n = n0 + r;
+                    Bs[b][kk][r] = (n < N && kg < K) ? We[size_t(b * N + n) * K + kg] : 0.0f;
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int kk = 0; kk < FK; ++kk) {
+                float av[4], bv[NB][4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) av[i] = As[kk][tr * 4 + i];
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) bv[b][j] = Bs[b][kk][tc * 4 + j];
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) acc[b][i][j] = __builtin_fmaf(av[i], bv[b][j], acc[b][i][j]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = m0 + tr * 4 + i;
+            if (row < 0 || row >= m_end) continue;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int col = n0 + tc * 4 + j;
+                if (col >= N) continue;
+                if (EPI == EPI_SWIGLU) {
+                    const float h = acc[0][i][j], u = acc[NB - 1][i][j];
+                    out[size_t(row) * N + col] = silu_f(h) * u;
+                    if (hu_save) {
+                        hu_save[size_t(row) * 2 * N + col] = h;
+                        hu_save[size_t(row) * 2 * N + N + col] = u;
+                    }
+                } else {
+                    out[size_t(row) * N + col] = acc[0][i][j];
+                }
+            }
+        }
+    }
+}
+
+int num_cus() {
+    static int n = 0;
+    static std::once_flag once;
+    std::call_once(once, [] {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            n = v;
+        else
+            n = 256;
+    });
+    return n;
+}
+
+bool set_lds_limits() {
+    static bool ok = false;
+    static std::once_flag once;
+    std::call_once(once, [] {
+        ok = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_bf16<EPI_SWIGLU>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, kLdsGemm) == hipSuccess &&
+             hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_bf16<EPI_PLAIN>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, kLdsGemm) == hipSuccess;
+    });
+    return ok;
+}
+
+// Workspace: [0, 4 KiB) tile map; then a [rows, F] in dtype.
+size_t ffn_ws_bytes(int32_t E, int64_t rows, int64_t F, moe_dtype_t dt) {
+    return align256(size_t(E + 1) * sizeof(int)) + align256(size_t(rows) * F * elt_size(dt));
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" size_t moe_expert_ffn_workspace_size(int32_t E, int64_t rows, int64_t d, int64_t F,
+                                                moe_dtype_t dtype) {
+    (void)d;
+    if (E <= 0 || rows < 0 || F <= 0 || !valid_dtype(dtype)) return 0;
+    return ffn_ws_bytes(E, rows, F, dtype);
+}
+
+extern "C" moe_status_t moe_expert_ffn(const void *x_disp, const int32_t *expert_off,
+                                       const void *w13, const void *w2, int32_t E, int64_t rows,
+                                       int64_t d, int64_t F, moe_dtype_t dtype, void *y_disp,
+                                       void *hu_save, void *ws, size_t ws_bytes, void *stream) {
+    if (!valid_dtype(dtype) || E <= 0 || rows < 0 || d <= 0 || F <= 0) return MOE_ERR_INVALID_ARG;
+    if (E > 1024 || rows >= (int64_t(1) << 31) || d > (1 << 20) || F > (1 << 20))
+        return MOE_ERR_UNSUPPORTED;
+    if (dtype == MOE_BF16 && (d % BK != 0 || F % BK != 0)) return MOE_ERR_UNSUPPORTED;
+    if (rows == 0) return MOE_OK;
+    if (!x_disp || !expert_off || !w13 || !w2 || !y_disp || !ws) return MOE_ERR_INVALID_ARG;
+    if (ws_bytes < ffn_ws_bytes(E, rows, F, dtype)) return MOE_ERR_CAPACITY;
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return MOE_ERR_ALIGN;
+    if ((d * elt_size(dtype)) % 16 != 0 || (F * elt_size(dtype)) % 16 != 0 || !aligned16(x_disp) ||
+        !aligned16(w13) || !aligned16(w2) || !aligned16(y_disp) || (hu_save && !aligned16(hu_save)))
+        return MOE_ERR_ALIGN;
+
+    const hipStream_t st = as_stream(stream);
+    char *wsb = static_cast<char *>(ws);
+    int *tile_off = reinterpret_cast<int *>(wsb);
+    void *act = wsb + align256(size_t(E + 1) * sizeof(int));
+
+    if (dtype == MOE_BF16) {
+        if (!set_lds_limits()) return MOE_ERR_HIP;
+        hipLaunchKernelGGL(k_tile_map, dim3(1), dim3(1024), 0, st, expert_off, E, BM, tile_off);
+        const int max_mt = int(cdiv(rows, BM)) + E;     // bound on sum_e ceil(M_e/BM)
+        const int nt1 = int(cdiv(F, BNW / 2)), nt2 = int(cdiv(d, BNW));
+        const int g1 = int(std::min<int64_t>(int64_t(max_mt) * nt1, num_cus()));
+        const int g2 = int(std::min<int64_t>(int64_t(max_mt) * nt2, num_cus()));
+        hipLaunchKernelGGL(k_gemm_bf16<EPI_SWIGLU>, dim3(g1), dim3(kGemmThreads), kLdsGemm, st,
+                           static_cast<const uint16_t *>(x_disp), expert_off, tile_off, E,
+                           static_cast<const uint16_t *>(w13), int(d), int(F), rows,
+                           static_cast<uint16_t *>(act), static_cast<uint16_t *>(hu_save), nt1);
+        hipLaunchKernelGGL(k_gemm_bf16<EPI_PLAIN>, dim3(g2), dim3(kGemmThreads), kLdsGemm, st,
+                           static_cast<const uint16_t *>(act), expert_off, tile_off, E,
+                           static_cast<const uint16_t *>(w2), int(F), int(d), rows,
+                           static_cast<uint16_t *>(y_disp), nullptr, nt2);
+        return launch_status();
+    }
+    // f32: the tile map uses FT-row tiles
+    hipLaunchKernelGGL(k_tile_map, dim3(1), dim3(1024), 0, st, expert_off, E, FT, tile_off);
+    const int max_mt = int(cdiv(rows, FT)) + E;
+    const int nt1 = int(cdiv(F, FT)), nt2 = int(cdiv(d, FT));
+    const int g1 = int(std::min<int64_t>(int64_t(max_mt) * nt1, 4 * num_cus()));
+    const int g2 = int(std::min<int64_t>(int64_t(max_mt) * nt2, 4 * num_cus()));
+    hipLaunchKernelGGL(k_gemm_f32<EPI_SWIGLU>, dim3(g1), dim3(256), 0, st,
+                       static_cast<const float *>(x_disp), expert_off, tile_off, E,
+                       static_cast<const float *>(w13), int(d), int(F), rows,
+                       static_cast<float *>(act), static_cast<float *>(hu_save), nt1);
+    hipLaunchKernelGGL(k_gemm_f32<EPI_PLAIN>, dim3(g2), dim3(256), 0, st,
+                       static_cast<const float *>(act), expert_off, tile_off, E,
+                       static_cast<const float *>(w2), int(F), int(d), rows,
+                       static_cast<float *>(y_disp), nullptr, nt2);
+    return launch_status();
+}
