@@ -150,10 +150,21 @@ moe_status_t moe_dispatch_status(const void *ws, void *stream);
  * [rows, d], rows >= expert_off[E] (the host cannot see expert_off: rows is the
  * allocation). float32 accumulation; bf16 stores round to nearest even (a is
  * stored in bf16 between the two GEMMs). hu_save [rows, 2F] (NULL: not written)
- * keeps h and u for the backward. Requires d % 64 == 0 and F % 64 == 0 for bf16.
- * ws: moe_expert_ffn_workspace_size() bytes. */
+ * keeps h and u for the backward. Requires d % 64 == 0 and F % 64 == 0 for bf16,
+ * E <= 1024. ws: moe_expert_ffn_workspace_size() bytes (it holds a), 256-byte
+ * aligned. */
 size_t moe_expert_ffn_workspace_size(int32_t E, int64_t rows, int64_t d, int64_t F,
                                      moe_dtype_t dtype);
+/* The two halves of moe_expert_ffn, one kernel each, for callers that schedule
+ * them separately (overlap, timing): gate_up writes act [rows, F] = silu(h) * u
+ * (and hu_save if non-NULL); down writes y_disp = act W2^T. No workspace. */
+moe_status_t moe_expert_ffn_gate_up(const void *x_disp, const int32_t *expert_off,
+                                    const void *w13, int32_t E, int64_t rows, int64_t d,
+                                    int64_t F, moe_dtype_t dtype, void *act, void *hu_save,
+                                    void *stream);
+moe_status_t moe_expert_ffn_down(const void *act, const int32_t *expert_off, const void *w2,
+                                 int32_t E, int64_t rows, int64_t d, int64_t F,
+                                 moe_dtype_t dtype, void *y_disp, void *stream);
 moe_status_t moe_expert_ffn(const void *x_disp, const int32_t *expert_off, const void *w13,
                             const void *w2, int32_t E, int64_t rows, int64_t d, int64_t F,
                             moe_dtype_t dtype, void *y_disp, void *hu_save, void *ws,

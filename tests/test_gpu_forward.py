@@ -254,3 +254,30 @@ def test_empty_and_tiny_inputs(gpu_lib):
     y = moe.moe_combine(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"), idx, g)
     torch.cuda.synchronize()
     assert y.shape == (0, 64)
+
+
+def test_split_ffn_calls_match_composite(gpu_lib):
+    """moe_expert_ffn_gate_up + moe_expert_ffn_down == moe_expert_ffn bit for bit,
+    and hu_save holds h and u (a = silu(h) * u recomputed from them agrees)."""
+    moe = gpu_lib
+    wl = _wl("mid_bf16", T=500, d=256, E=16, k=4, F=192)
+    inp = moe_synth.layer_inputs(wl, device="cuda")
+    idx, gates, _ = moe.moe_route(inp["x"], inp["w_router"], wl.k)
+    plan = moe.moe_dispatch(inp["x"], idx, wl.E)
+    hu = torch.empty((wl.pairs, 2 * wl.F), dtype=torch.bfloat16, device="cuda")
+    y1 = moe.moe_expert_ffn(plan["x_disp"], plan["expert_off"], inp["w13"], inp["w2"], hu_save=hu)
+    act = moe.moe_expert_ffn_gate_up(plan["x_disp"], plan["expert_off"], inp["w13"])
+    y2 = moe.moe_expert_ffn_down(act, plan["expert_off"], inp["w2"])
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    h, u = hu[:, :wl.F].float(), hu[:, wl.F:].float()
+    a_ref = torch.nn.functional.silu(h) * u
+    assert oracle.normwise_rel_err(_np(act), a_ref.cpu().numpy()) <= BF16_TOL
+    ref = oracle.forward(inp["x"].cpu(), inp["w_router"].cpu(), inp["w13"].cpu(), inp["w2"].cpu(), wl.k)
+    F = wl.F
+    x_disp = ref["x_disp"].astype(np.float64)
+    w13 = inp["w13"].double().cpu().numpy()
+    for e in (0, 7, 15):
+        a, b = ref["expert_off"][e], ref["expert_off"][e + 1]
+        h_ref = x_disp[a:b] @ w13[e, :F].T
+        assert oracle.normwise_rel_err(_np(hu[a:b, :F]), h_ref) <= BF16_TOL

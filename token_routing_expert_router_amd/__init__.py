@@ -18,7 +18,8 @@ from typing import Optional
 import torch
 
 __all__ = ["MoEError", "load", "library_path", "moe_abi_version", "moe_route", "moe_dispatch",
-           "moe_dispatch_status", "moe_expert_ffn", "moe_combine", "moe_combine_bwd",
+           "moe_dispatch_status", "moe_expert_ffn", "moe_expert_ffn_gate_up",
+           "moe_expert_ffn_down", "moe_combine", "moe_combine_bwd",
            "moe_expert_ffn_bwd", "moe_route_bwd", "moe_dispatch_bwd", "Layout", "forward",
            "EXPORTED"]
 
@@ -45,6 +46,8 @@ EXPORTED = {
     "moe_expert_ffn_workspace_size": (_SZ, [_I32, _I64, _I64, _I64, _I32]),
     "moe_expert_ffn": (_I32, [_P, _P, _P, _P, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _SZ,
                               _P]),
+    "moe_expert_ffn_gate_up": (_I32, [_P, _P, _P, _I32, _I64, _I64, _I64, _I32, _P, _P, _P]),
+    "moe_expert_ffn_down": (_I32, [_P, _P, _P, _I32, _I64, _I64, _I64, _I32, _P, _P]),
     "moe_combine": (_I32, [_P, _P, _P, _I64, _I32, _I64, _I64, _I32, _P, _P]),
     "moe_combine_bwd": (_I32, [_P, _P, _P, _P, _I64, _I32, _I64, _I64, _I32, _P, _P, _P]),
     "moe_expert_ffn_bwd_workspace_size": (_SZ, [_I32, _I64, _I64, _I64, _I32]),
@@ -200,6 +203,29 @@ def moe_expert_ffn(x_disp, expert_off, w13, w2, *, y_disp=None, hu_save=None, ws
     _check("moe_expert_ffn", lib.moe_expert_ffn(
         _ptr(x_disp), _ptr(expert_off), _ptr(w13), _ptr(w2), E, rows, d, F, _dt(x_disp),
         _ptr(y_disp), _ptr(hu_save), _ptr(ws), ws.numel(), _stream(stream)))
+    return y_disp
+
+
+def moe_expert_ffn_gate_up(x_disp, expert_off, w13, *, act=None, hu_save=None, stream=None):
+    rows, d = x_disp.shape
+    E, F2, _ = w13.shape
+    F = F2 // 2
+    if act is None:
+        act = torch.empty((rows, F), dtype=x_disp.dtype, device=x_disp.device)
+    _check("moe_expert_ffn_gate_up", load().moe_expert_ffn_gate_up(
+        _ptr(x_disp), _ptr(expert_off), _ptr(w13), E, rows, d, F, _dt(x_disp), _ptr(act),
+        _ptr(hu_save), _stream(stream)))
+    return act
+
+
+def moe_expert_ffn_down(act, expert_off, w2, *, y_disp=None, stream=None):
+    rows, F = act.shape
+    E, d, _ = w2.shape
+    if y_disp is None:
+        y_disp = torch.empty((rows, d), dtype=act.dtype, device=act.device)
+    _check("moe_expert_ffn_down", load().moe_expert_ffn_down(
+        _ptr(act), _ptr(expert_off), _ptr(w2), E, rows, d, F, _dt(act), _ptr(y_disp),
+        _stream(stream)))
     return y_disp
 
 

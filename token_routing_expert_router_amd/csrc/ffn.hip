@@ -45,39 +45,62 @@ __device__ __forceinline__ int swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 
 
 __device__ __forceinline__ float silu_f(float h) { return h / (1.0f + __expf(-h)); }
 
-// m-tiles per expert, prefix summed: tile_off[e] = sum_{e'<e} ceil(M_e'/tile_rows).
-__global__ void k_tile_map(const int *__restrict__ expert_off, int E, int tile_rows,
-                           int *__restrict__ tile_off) {
-    __shared__ int buf[1024];
-    const int tid = threadIdx.x;
-    int v = 0;
-    if (tid < E) v = (max(expert_off[tid + 1] - expert_off[tid], 0) + tile_rows - 1) / tile_rows;
-    const int own = v;
-    for (int off = 1; off < 1024; off <<= 1) {
-        buf[tid] = v;
+// m-tiles per expert, prefix summed into LDS by every workgroup:
+// toff[e] = sum_{e'<e} ceil(M_e'/tile_rows), toff[E] = total (E <= 1024, 256 threads).
+// Doing it in the kernel keeps the grouped GEMM a single launch.
+constexpr int kMaxE = 1024;
+__device__ __forceinline__ void build_tile_map(const int *__restrict__ expert_off, int E,
+                                               int tile_rows, int64_t rows_alloc, int *toff,
+                                               int *scratch /* [256] */) {
+    const int tid = threadIdx.x;     // blockDim.x == 256
+    int cnt[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = tid * 4 + i;
+        int c = 0;
+        if (e < E) {
+            const int64_t a = min<int64_t>(expert_off[e], rows_alloc);
+            const int64_t b = min<int64_t>(expert_off[e + 1], rows_alloc);
+            c = b > a ? int((b - a + tile_rows - 1) / tile_rows) : 0;
+        }
+        cnt[i] = c;
+        sum += c;
+    }
+    int v = sum;
+    for (int off = 1; off < 256; off <<= 1) {
+        scratch[tid] = v;
         __syncthreads();
-        if (tid >= off) v += buf[tid - off];
+        if (tid >= off) v += scratch[tid - off];
         __syncthreads();
     }
-    if (tid < E) tile_off[tid] = v - own;
-    if (tid == E - 1) tile_off[E] = v;
+    int run = v - sum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = tid * 4 + i;
+        if (e < E) toff[e] = run;
+        run += cnt[i];
+    }
+    if (tid == 255) toff[E] = v;     // inclusive sum of the last thread = total
+    __syncthreads();
 }
 
 template <int EPI>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm_bf16(
     const uint16_t *__restrict__ A,        // [rows, K]
     const int *__restrict__ expert_off,    // [E+1]
-    const int *__restrict__ tile_off,      // [E+1]
     int E, const uint16_t *__restrict__ W, // [E, Nw, K]
     int K, int N, int64_t rows_alloc,
     uint16_t *__restrict__ out,            // [rows, N]
     uint16_t *__restrict__ hu_save,        // [rows, 2N] (gate/up only; may be null)
     int n_tiles) {
     extern __shared__ __align__(16) unsigned char lds[];
+    __shared__ int tile_off[kMaxE + 1];
+    __shared__ int map_scratch[256];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int Nw = (EPI == EPI_SWIGLU) ? 2 * N : N;   // weight rows per expert
+    build_tile_map(expert_off, E, BM, rows_alloc, tile_off, map_scratch);
     const int total = tile_off[E] * n_tiles;
     const int G = gridDim.x;
     // this workgroup's place in a round: XCD (blockIdx % 8) gets a contiguous run
@@ -247,17 +270,19 @@ constexpr int FT = 64, FK = 16;
 
 template <int EPI>
 __global__ __launch_bounds__(256) void k_gemm_f32(const float *__restrict__ A,
-                                                  const int *__restrict__ expert_off,
-                                                  const int *__restrict__ tile_off, int E,
+                                                  const int *__restrict__ expert_off, int E,
                                                   const float *__restrict__ W, int K, int N,
                                                   int64_t rows_alloc, float *__restrict__ out,
                                                   float *__restrict__ hu_save, int n_tiles) {
     constexpr int NB = (EPI == EPI_SWIGLU) ? 2 : 1;   // weight tiles (W1, W3)
     __shared__ float As[FK][FT + 1];
     __shared__ float Bs[NB][FK][FT + 1];
+    __shared__ int tile_off[kMaxE + 1];
+    __shared__ int map_scratch[256];
     const int tid = threadIdx.x;
     const int tr = tid / 16, tc = tid % 16;
     const int Nw = NB * N;
+    build_tile_map(expert_off, E, FT, rows_alloc, tile_off, map_scratch);
     const int total = tile_off[E] * n_tiles;
     for (int item = blockIdx.x; item < total; item += gridDim.x) {
         const int mt = item / n_tiles, nt = item % n_tiles;
@@ -351,9 +376,62 @@ bool set_lds_limits() {
     return ok;
 }
 
-// Workspace: [0, 4 KiB) tile map; then a [rows, F] in dtype.
-size_t ffn_ws_bytes(int32_t E, int64_t rows, int64_t F, moe_dtype_t dt) {
-    return align256(size_t(E + 1) * sizeof(int)) + align256(size_t(rows) * F * elt_size(dt));
+// Workspace of the composite call: the activation a [rows, F] in dtype.
+size_t ffn_ws_bytes(int64_t rows, int64_t F, moe_dtype_t dt) {
+    return align256(size_t(rows) * F * elt_size(dt));
+}
+
+moe_status_t check_common(int32_t E, int64_t rows, int64_t d, int64_t F, moe_dtype_t dtype) {
+    if (!valid_dtype(dtype) || E <= 0 || rows < 0 || d <= 0 || F <= 0) return MOE_ERR_INVALID_ARG;
+    if (E > kMaxE || rows >= (int64_t(1) << 31) || d > (1 << 20) || F > (1 << 20))
+        return MOE_ERR_UNSUPPORTED;
+    if (dtype == MOE_BF16 && (d % BK != 0 || F % BK != 0)) return MOE_ERR_UNSUPPORTED;
+    if ((d * elt_size(dtype)) % 16 != 0 || (F * elt_size(dtype)) % 16 != 0) return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+
+moe_status_t launch_gate_up(const void *x_disp, const int32_t *expert_off, const void *w13,
+                            int32_t E, int64_t rows, int64_t d, int64_t F, moe_dtype_t dtype,
+                            void *act, void *hu_save, hipStream_t st) {
+    if (dtype == MOE_BF16) {
+        if (!set_lds_limits()) return MOE_ERR_HIP;
+        const int nt = int(cdiv(F, BNW / 2));
+        const int g = int(std::min<int64_t>((cdiv(rows, BM) + E) * nt, num_cus()));
+        hipLaunchKernelGGL(k_gemm_bf16<EPI_SWIGLU>, dim3(g), dim3(kGemmThreads), kLdsGemm, st,
+                           static_cast<const uint16_t *>(x_disp), expert_off, E,
+                           static_cast<const uint16_t *>(w13), int(d), int(F), rows,
+                           static_cast<uint16_t *>(act), static_cast<uint16_t *>(hu_save), nt);
+    } else {
+        const int nt = int(cdiv(F, FT));
+        const int g = int(std::min<int64_t>((cdiv(rows, FT) + E) * nt, 4 * num_cus()));
+        hipLaunchKernelGGL(k_gemm_f32<EPI_SWIGLU>, dim3(g), dim3(256), 0, st,
+                           static_cast<const float *>(x_disp), expert_off, E,
+                           static_cast<const float *>(w13), int(d), int(F), rows,
+                           static_cast<float *>(act), static_cast<float *>(hu_save), nt);
+    }
+    return launch_status();
+}
+
+moe_status_t launch_down(const void *act, const int32_t *expert_off, const void *w2, int32_t E,
+                         int64_t rows, int64_t d, int64_t F, moe_dtype_t dtype, void *y_disp,
+                         hipStream_t st) {
+    if (dtype == MOE_BF16) {
+        if (!set_lds_limits()) return MOE_ERR_HIP;
+        const int nt = int(cdiv(d, BNW));
+        const int g = int(std::min<int64_t>((cdiv(rows, BM) + E) * nt, num_cus()));
+        hipLaunchKernelGGL(k_gemm_bf16<EPI_PLAIN>, dim3(g), dim3(kGemmThreads), kLdsGemm, st,
+                           static_cast<const uint16_t *>(act), expert_off, E,
+                           static_cast<const uint16_t *>(w2), int(F), int(d), rows,
+                           static_cast<uint16_t *>(y_disp), nullptr, nt);
+    } else {
+        const int nt = int(cdiv(d, FT));
+        const int g = int(std::min<int64_t>((cdiv(rows, FT) + E) * nt, 4 * num_cus()));
+        hipLaunchKernelGGL(k_gemm_f32<EPI_PLAIN>, dim3(g), dim3(256), 0, st,
+                           static_cast<const float *>(act), expert_off, E,
+                           static_cast<const float *>(w2), int(F), int(d), rows,
+                           static_cast<float *>(y_disp), nullptr, nt);
+    }
+    return launch_status();
 }
 
 }  // namespace
@@ -365,60 +443,51 @@ extern "C" size_t moe_expert_ffn_workspace_size(int32_t E, int64_t rows, int64_t
                                                 moe_dtype_t dtype) {
     (void)d;
     if (E <= 0 || rows < 0 || F <= 0 || !valid_dtype(dtype)) return 0;
-    return ffn_ws_bytes(E, rows, F, dtype);
+    return ffn_ws_bytes(rows, F, dtype);
+}
+
+extern "C" moe_status_t moe_expert_ffn_gate_up(const void *x_disp, const int32_t *expert_off,
+                                               const void *w13, int32_t E, int64_t rows,
+                                               int64_t d, int64_t F, moe_dtype_t dtype, void *act,
+                                               void *hu_save, void *stream) {
+    const moe_status_t c = check_common(E, rows, d, F, dtype);
+    if (c != MOE_OK) return c;
+    if (rows == 0) return MOE_OK;
+    if (!x_disp || !expert_off || !w13 || !act) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x_disp) || !aligned16(w13) || !aligned16(act) || (hu_save && !aligned16(hu_save)))
+        return MOE_ERR_ALIGN;
+    return launch_gate_up(x_disp, expert_off, w13, E, rows, d, F, dtype, act, hu_save,
+                          as_stream(stream));
+}
+
+extern "C" moe_status_t moe_expert_ffn_down(const void *act, const int32_t *expert_off,
+                                            const void *w2, int32_t E, int64_t rows, int64_t d,
+                                            int64_t F, moe_dtype_t dtype, void *y_disp,
+                                            void *stream) {
+    const moe_status_t c = check_common(E, rows, d, F, dtype);
+    if (c != MOE_OK) return c;
+    if (rows == 0) return MOE_OK;
+    if (!act || !expert_off || !w2 || !y_disp) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(act) || !aligned16(w2) || !aligned16(y_disp)) return MOE_ERR_ALIGN;
+    return launch_down(act, expert_off, w2, E, rows, d, F, dtype, y_disp, as_stream(stream));
 }
 
 extern "C" moe_status_t moe_expert_ffn(const void *x_disp, const int32_t *expert_off,
                                        const void *w13, const void *w2, int32_t E, int64_t rows,
                                        int64_t d, int64_t F, moe_dtype_t dtype, void *y_disp,
                                        void *hu_save, void *ws, size_t ws_bytes, void *stream) {
-    if (!valid_dtype(dtype) || E <= 0 || rows < 0 || d <= 0 || F <= 0) return MOE_ERR_INVALID_ARG;
-    if (E > 1024 || rows >= (int64_t(1) << 31) || d > (1 << 20) || F > (1 << 20))
-        return MOE_ERR_UNSUPPORTED;
-    if (dtype == MOE_BF16 && (d % BK != 0 || F % BK != 0)) return MOE_ERR_UNSUPPORTED;
+    const moe_status_t c = check_common(E, rows, d, F, dtype);
+    if (c != MOE_OK) return c;
     if (rows == 0) return MOE_OK;
     if (!x_disp || !expert_off || !w13 || !w2 || !y_disp || !ws) return MOE_ERR_INVALID_ARG;
-    if (ws_bytes < ffn_ws_bytes(E, rows, F, dtype)) return MOE_ERR_CAPACITY;
+    if (ws_bytes < ffn_ws_bytes(rows, F, dtype)) return MOE_ERR_CAPACITY;
     if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return MOE_ERR_ALIGN;
-    if ((d * elt_size(dtype)) % 16 != 0 || (F * elt_size(dtype)) % 16 != 0 || !aligned16(x_disp) ||
-        !aligned16(w13) || !aligned16(w2) || !aligned16(y_disp) || (hu_save && !aligned16(hu_save)))
+    if (!aligned16(x_disp) || !aligned16(w13) || !aligned16(w2) || !aligned16(y_disp) ||
+        (hu_save && !aligned16(hu_save)))
         return MOE_ERR_ALIGN;
-
     const hipStream_t st = as_stream(stream);
-    char *wsb = static_cast<char *>(ws);
-    int *tile_off = reinterpret_cast<int *>(wsb);
-    void *act = wsb + align256(size_t(E + 1) * sizeof(int));
-
-    if (dtype == MOE_BF16) {
-        if (!set_lds_limits()) return MOE_ERR_HIP;
-        hipLaunchKernelGGL(k_tile_map, dim3(1), dim3(1024), 0, st, expert_off, E, BM, tile_off);
-        const int max_mt = int(cdiv(rows, BM)) + E;     // bound on sum_e ceil(M_e/BM)
-        const int nt1 = int(cdiv(F, BNW / 2)), nt2 = int(cdiv(d, BNW));
-        const int g1 = int(std::min<int64_t>(int64_t(max_mt) * nt1, num_cus()));
-        const int g2 = int(std::min<int64_t>(int64_t(max_mt) * nt2, num_cus()));
-        hipLaunchKernelGGL(k_gemm_bf16<EPI_SWIGLU>, dim3(g1), dim3(kGemmThreads), kLdsGemm, st,
-                           static_cast<const uint16_t *>(x_disp), expert_off, tile_off, E,
-                           static_cast<const uint16_t *>(w13), int(d), int(F), rows,
-                           static_cast<uint16_t *>(act), static_cast<uint16_t *>(hu_save), nt1);
-        hipLaunchKernelGGL(k_gemm_bf16<EPI_PLAIN>, dim3(g2), dim3(kGemmThreads), kLdsGemm, st,
-                           static_cast<const uint16_t *>(act), expert_off, tile_off, E,
-                           static_cast<const uint16_t *>(w2), int(F), int(d), rows,
-                           static_cast<uint16_t *>(y_disp), nullptr, nt2);
-        return launch_status();
-    }
-    // f32: the tile map uses FT-row tiles
-    hipLaunchKernelGGL(k_tile_map, dim3(1), dim3(1024), 0, st, expert_off, E, FT, tile_off);
-    const int max_mt = int(cdiv(rows, FT)) + E;
-    const int nt1 = int(cdiv(F, FT)), nt2 = int(cdiv(d, FT));
-    const int g1 = int(std::min<int64_t>(int64_t(max_mt) * nt1, 4 * num_cus()));
-    const int g2 = int(std::min<int64_t>(int64_t(max_mt) * nt2, 4 * num_cus()));
-    hipLaunchKernelGGL(k_gemm_f32<EPI_SWIGLU>, dim3(g1), dim3(256), 0, st,
-                       static_cast<const float *>(x_disp), expert_off, tile_off, E,
-                       static_cast<const float *>(w13), int(d), int(F), rows,
-                       static_cast<float *>(act), static_cast<float *>(hu_save), nt1);
-    hipLaunchKernelGGL(k_gemm_f32<EPI_PLAIN>, dim3(g2), dim3(256), 0, st,
-                       static_cast<const float *>(act), expert_off, tile_off, E,
-                       static_cast<const float *>(w2), int(F), int(d), rows,
-                       static_cast<float *>(y_disp), nullptr, nt2);
-    return launch_status();
+    const moe_status_t s1 = launch_gate_up(x_disp, expert_off, w13, E, rows, d, F, dtype, ws,
+                                           hu_save, st);
+    if (s1 != MOE_OK) return s1;
+    return launch_down(ws, expert_off, w2, E, rows, d, F, dtype, y_disp, st);
 }
