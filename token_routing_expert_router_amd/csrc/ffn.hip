@@ -29,7 +29,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128;         // token rows per tile
+constexpr int BM = 256;         // token rows per tile
 constexpr int BNW = 256;        // weight rows per tile
 constexpr int BK = 64;          // depth per LDS stage
 constexpr int kGemmThreads = 256;
@@ -84,181 +84,226 @@ __device__ __forceinline__ void build_tile_map(const int *__restrict__ expert_of
     __syncthreads();
 }
 
+// Per-item state of the bf16 grouped GEMM: uniform bases, per-lane byte offsets of
+// the lane's 16-byte chunk in each of its wave's 8 A groups and 8 B groups.
+struct GemmItem {
+    const char *Ab;          // first token row of the tile
+    const char *Wb;          // expert's weight panel
+    uint32_t a_off[8], b_off[8];
+    int a_groups;            // A groups (of 8 rows) holding live rows
+    int64_t m0, m_end;       // token rows [m0, m_end) are live in this tile
+    int n0;                  // first output column
+};
+
+// Direct global->LDS loads of one stage: wave w moves A groups w*8..w*8+7 and B
+// groups w*8..w*8+7, each one 1 KiB wavefront instruction.
+__device__ __forceinline__ void issue_stage(unsigned char *lds, int stage, int k0,
+                                            const GemmItem &it, int wave) {
+    unsigned char *As = lds + stage * (kLdsA + kLdsB);
+    unsigned char *Bs = As + kLdsA;
+    const char *Ak = it.Ab + size_t(k0) * 2;
+    const char *Wk = it.Wb + size_t(k0) * 2;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (j < it.a_groups)
+            __builtin_amdgcn_global_load_lds(
+                Ak + it.a_off[j], (__attribute__((address_space(3))) void *)(As + (wave * 8 + j) * 1024),
+                16, 0, 0);
+        __builtin_amdgcn_global_load_lds(
+            Wk + it.b_off[j], (__attribute__((address_space(3))) void *)(Bs + (wave * 8 + j) * 1024),
+            16, 0, 0);
+    }
+}
+
+// LDS reads of one k16 step: the wave's two weight fragments and NS token fragments
+// (16 bytes per lane each; rows are 128 B with chunk c stored at c ^ swz(row)).
+template <int NS>
+__device__ __forceinline__ void read_frags(const unsigned char *As, const unsigned char *Bs,
+                                           int lane, int ks, const int (&brow)[2],
+                                           bf16x8 (&wf)[2], bf16x8 (&tf)[NS]) {
+    const int kc = ks * 2 + (lane >> 5);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int r = brow[s] + (lane & 31);
+        wf[s] = *reinterpret_cast<const bf16x8 *>(Bs + r * 128 + ((kc ^ swz(r)) << 4));
+    }
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        const int r = i * 32 + (lane & 31);
+        tf[i] = *reinterpret_cast<const bf16x8 *>(As + r * 128 + ((kc ^ swz(r)) << 4));
+    }
+}
+
+// One work item with NS live 32-row token sub-tiles: the whole K loop and the
+// epilogue, branch-free in the inner loop.
+template <int EPI, int NS>
+__device__ __forceinline__ void run_item(unsigned char *lds, const GemmItem &it, int wave,
+                                         int lane, int K, int N, uint16_t *__restrict__ out,
+                                         uint16_t *__restrict__ hu_save) {
+    f32x16 acc[NS][2];
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    // B rows of this wave's two 32-row weight sub-tiles: gate/up pairs W1 rows with
+    // the same W3 rows; down takes 64 consecutive W2 rows
+    int brow[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+        brow[s] = (EPI == EPI_SWIGLU) ? s * 128 + wave * 32 : wave * 64 + s * 32;
+
+    const int KT = K / BK;
+    __syncthreads();                 // the previous item's readers are done with LDS
+    issue_stage(lds, 0, 0, it, wave);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < KT) issue_stage(lds, cur ^ 1, (kt + 1) * BK, it, wave);
+        const unsigned char *As = lds + cur * (kLdsA + kLdsB);
+        const unsigned char *Bs = As + kLdsA;
+        // fragments double-buffered across the four k16 steps: the LDS reads of step
+        // ks+1 are issued before the MFMAs of step ks (sched_barrier keeps that order)
+        bf16x8 wf[2][2], tf[2][NS];
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            if (ks == 0) {
+                read_frags<NS>(As, Bs, lane, 0, brow, wf[0], tf[0]);
+            }
+            if (ks + 1 < BK / 16) read_frags<NS>(As, Bs, lane, ks + 1, brow, wf[(ks + 1) & 1], tf[(ks + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < NS; ++i)
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    acc[i][s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks & 1][s], tf[ks & 1][i], acc[i][s], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the next stage landed
+        __syncthreads();                 // everyone's loads landed, and cur is free
+    }
+
+    // epilogue: D = W_tile * X_tile^T, so lane l holds token column m = l & 31 and, for
+    // v = 4g + q, weight row n = 8g + 4*(l >> 5) + q: four consecutive outputs of one
+    // token row, stored as one 8-byte write per (sub-tile, g)
+    const int64_t mrow0 = it.m0 + (lane & 31);
+    const int nl = 4 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        const int64_t m = mrow0 + i * 32;
+        if (m >= it.m_end) continue;
+        if (EPI == EPI_SWIGLU) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = it.n0 + wave * 32 + 8 * g + nl;
+                if (n >= N) continue;
+                float a4[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) a4[q] = silu_f(acc[i][0][4 * g + q]) * acc[i][1][4 * g + q];
+                uint2 pa;
+                pa.x = pack_bf16x2(a4[0], a4[1]);
+                pa.y = pack_bf16x2(a4[2], a4[3]);
+                *reinterpret_cast<uint2 *>(out + m * N + n) = pa;
+                if (hu_save) {
+                    uint2 ph, pu;
+                    ph.x = pack_bf16x2(acc[i][0][4 * g], acc[i][0][4 * g + 1]);
+                    ph.y = pack_bf16x2(acc[i][0][4 * g + 2], acc[i][0][4 * g + 3]);
+                    pu.x = pack_bf16x2(acc[i][1][4 * g], acc[i][1][4 * g + 1]);
+                    pu.y = pack_bf16x2(acc[i][1][4 * g + 2], acc[i][1][4 * g + 3]);
+                    *reinterpret_cast<uint2 *>(hu_save + m * 2 * N + n) = ph;
+                    *reinterpret_cast<uint2 *>(hu_save + m * 2 * N + N + n) = pu;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int n = it.n0 + wave * 64 + s * 32 + 8 * g + nl;
+                    if (n >= N) continue;
+                    uint2 p;
+                    p.x = pack_bf16x2(acc[i][s][4 * g], acc[i][s][4 * g + 1]);
+                    p.y = pack_bf16x2(acc[i][s][4 * g + 2], acc[i][s][4 * g + 3]);
+                    *reinterpret_cast<uint2 *>(out + m * N + n) = p;
+                }
+        }
+    }
+}
+
 template <int EPI>
-__global__ __launch_bounds__(kGemmThreads) void k_gemm_bf16(
-    const uint16_t *__restrict__ A,        // [rows, K]
+__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_bf16(
+    const uint16_t *__restrict__ A,        // token rows [rows, K]
     const int *__restrict__ expert_off,    // [E+1]
     int E, const uint16_t *__restrict__ W, // [E, Nw, K]
     int K, int N, int64_t rows_alloc,
     uint16_t *__restrict__ out,            // [rows, N]
     uint16_t *__restrict__ hu_save,        // [rows, 2N] (gate/up only; may be null)
     int n_tiles) {
-    extern __shared__ __align__(16) unsigned char lds[];
+    extern __shared__ __align__(16) unsigned char lds[];   // 2 stages x (A 32 KiB + B 32 KiB)
     __shared__ int tile_off[kMaxE + 1];
     __shared__ int map_scratch[256];
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int Nw = (EPI == EPI_SWIGLU) ? 2 * N : N;   // weight rows per expert
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wavefront
+    const int Nw = (EPI == EPI_SWIGLU) ? 2 * N : N;              // weight rows per expert
     build_tile_map(expert_off, E, BM, rows_alloc, tile_off, map_scratch);
     const int total = tile_off[E] * n_tiles;
     const int G = gridDim.x;
     // this workgroup's place in a round: XCD (blockIdx % 8) gets a contiguous run
     const int per = G / 8;
     const int slot = (G % 8 == 0) ? (blockIdx.x % 8) * per + blockIdx.x / 8 : blockIdx.x;
+    // A direct load puts lane l's 16 bytes at row l/8, physical chunk l%8 of its
+    // 8-row group, so the XOR swizzle is applied on the global side
+    const int lrow = lane >> 3;
+    const int pchunk = lane & 7;
 
     for (int base = 0; base < total; base += G) {
         const int item = base + slot;
         if (item >= total) break;
         const int mt = item / n_tiles, nt = item % n_tiles;
-        // expert owning m-tile mt: largest e with tile_off[e] <= mt
-        int lo = 0, hi = E;
+        int lo = 0, hi = E;                          // expert owning m-tile mt
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
             if (tile_off[mid] <= mt) lo = mid; else hi = mid;
         }
         const int e = lo;
-        const int m0 = expert_off[e] + (mt - tile_off[e]) * BM;
+        GemmItem it;
+        it.m0 = int64_t(expert_off[e]) + int64_t(mt - tile_off[e]) * BM;
         // rows past the allocation are never written, whatever expert_off holds
-        const int m_end = int(min<int64_t>(expert_off[e + 1], rows_alloc));
-        const int n0 = nt * (EPI == EPI_SWIGLU ? BNW / 2 : BNW);
-        const uint16_t *We = W + size_t(e) * Nw * K;
-
-        // global source rows of this thread's chunks (clamped: out-of-range rows
-        // compute garbage that is never stored)
-        const uint16_t *a_src[4];
-        const uint16_t *b_src[8];
+        it.m_end = min<int64_t>(expert_off[e + 1], rows_alloc);
+        it.n0 = nt * (EPI == EPI_SWIGLU ? BNW / 2 : BNW);
+        it.Ab = reinterpret_cast<const char *>(A + it.m0 * K);
+        it.Wb = reinterpret_cast<const char *>(W + size_t(e) * Nw * K);
+        it.a_groups = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + i * kGemmThreads;
-            int64_t r = int64_t(m0) + c / 8;
-            if (r >= rows_alloc) r = rows_alloc - 1;
-            if (r < 0) r = 0;
-            a_src[i] = A + r * K + (c % 8) * 8;
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = tid + i * kGemmThreads;
-            const int br = c / 8;
+        for (int j = 0; j < 8; ++j) {
+            const int g = wave * 8 + j;
+            const int r = g * 8 + lrow;              // tile row 0..255
+            const int c = pchunk ^ swz(r);
+            const int64_t tr = min<int64_t>(it.m0 + r, rows_alloc - 1);
+            it.a_off[j] = uint32_t(((tr - it.m0) * K + c * 8) * 2);
+            if (it.m0 + g * 8 < it.m_end) it.a_groups = j + 1;
             int wr;
             if (EPI == EPI_SWIGLU) {
-                const int n = min(n0 + (br & 127), N - 1);
-                wr = (br < 128) ? n : N + n;
+                const int n = min(it.n0 + (r & 127), N - 1);
+                wr = (r < 128) ? n : N + n;
             } else {
-                wr = min(n0 + br, N - 1);
+                wr = min(it.n0 + r, N - 1);
             }
-            b_src[i] = We + size_t(wr) * K + (c % 8) * 8;
+            it.b_off[j] = uint32_t((size_t(wr) * K + c * 8) * 2);
         }
-        u32x4 ra[4], rb[8];
-#define MOE_GLOAD(k0)                                                                   \
-    do {                                                                                \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i)                                   \
-            ra[i] = *reinterpret_cast<const u32x4 *>(a_src[i] + (k0));                  \
-        _Pragma("unroll") for (int i = 0; i < 8; ++i)                                   \
-            rb[i] = *reinterpret_cast<const u32x4 *>(b_src[i] + (k0));                  \
-    } while (0)
-#define MOE_LSTORE(buf)                                                                 \
-    do {                                                                                \
-        unsigned char *As_ = lds + (buf) * (kLdsA + kLdsB);                             \
-        unsigned char *Bs_ = As_ + kLdsA;                                               \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                 \
-            const int c = tid + i * kGemmThreads, r = c / 8, kc = c % 8;                \
-            *reinterpret_cast<u32x4 *>(As_ + r * 128 + ((kc ^ swz(r)) << 4)) = ra[i];   \
-        }                                                                               \
-        _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                 \
-            const int c = tid + i * kGemmThreads, r = c / 8, kc = c % 8;                \
-            *reinterpret_cast<u32x4 *>(Bs_ + r * 128 + ((kc ^ swz(r)) << 4)) = rb[i];   \
-        }                                                                               \
-    } while (0)
-
-        f32x16 acc[2][4];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-        // B rows of this wave's four 32-row sub-tiles
-        int brow[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-            brow[s] = (EPI == EPI_SWIGLU) ? (s >> 1) * 128 + wn * 64 + (s & 1) * 32
-                                          : wn * 128 + s * 32;
-
-        const int KT = K / BK;
-        __syncthreads();          // previous item's readers are done with LDS
-        MOE_GLOAD(0);
-        MOE_LSTORE(0);
-        __syncthreads();
-        for (int kt = 0; kt < KT; ++kt) {
-            const int cur = kt & 1;
-            if (kt + 1 < KT) MOE_GLOAD((kt + 1) * BK);
-            const unsigned char *As = lds + cur * (kLdsA + kLdsB);
-            const unsigned char *Bs = As + kLdsA;
-#pragma unroll
-            for (int ks = 0; ks < BK / 16; ++ks) {
-                const int kc = ks * 2 + (lane >> 5);
-                bf16x8 af[2], bfr[4];
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int r = wm * 64 + i * 32 + (lane & 31);
-                    af[i] = *reinterpret_cast<const bf16x8 *>(As + r * 128 + ((kc ^ swz(r)) << 4));
-                }
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int r = brow[s] + (lane & 31);
-                    bfr[s] = *reinterpret_cast<const bf16x8 *>(Bs + r * 128 + ((kc ^ swz(r)) << 4));
-                }
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int s = 0; s < 4; ++s)
-                        acc[i][s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[s], acc[i][s], 0, 0, 0);
-            }
-            if (kt + 1 < KT) MOE_LSTORE(cur ^ 1);
-            __syncthreads();
-        }
-
-#undef MOE_GLOAD
-#undef MOE_LSTORE
-        // epilogue: lane holds column (lane & 31) of each 32x32 sub-tile and rows
-        // 8*(v/4) + 4*(lane/32) + v%4 for v = 0..15
-        const int col_l = lane & 31;
-        const int row_l = 4 * (lane >> 5);
-        if (EPI == EPI_SWIGLU) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    const int col = n0 + wn * 64 + s2 * 32 + col_l;
-                    if (col >= N) continue;
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + row_l + (v & 3);
-                        if (row < 0 || row >= m_end) continue;
-                        const float h = acc[i][s2][v], u = acc[i][s2 + 2][v];
-                        out[size_t(row) * N + col] = f32_to_bf16_bits(silu_f(h) * u);
-                        if (hu_save) {
-                            hu_save[size_t(row) * 2 * N + col] = f32_to_bf16_bits(h);
-                            hu_save[size_t(row) * 2 * N + N + col] = f32_to_bf16_bits(u);
-                        }
-                    }
-                }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int col = n0 + wn * 128 + s * 32 + col_l;
-                    if (col >= N) continue;
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + row_l + (v & 3);
-                        if (row < 0 || row >= m_end) continue;
-                        out[size_t(row) * N + col] = f32_to_bf16_bits(acc[i][s][v]);
-                    }
-                }
+        const int nsub = int(min<int64_t>(8, (it.m_end - it.m0 + 31) / 32));
+        switch (nsub) {
+        case 8: run_item<EPI, 8>(lds, it, wave, lane, K, N, out, hu_save); break;
+        case 7: run_item<EPI, 7>(lds, it, wave, lane, K, N, out, hu_save); break;
+        case 6: run_item<EPI, 6>(lds, it, wave, lane, K, N, out, hu_save); break;
+        case 5: run_item<EPI, 5>(lds, it, wave, lane, K, N, out, hu_save); break;
+        case 4: run_item<EPI, 4>(lds, it, wave, lane, K, N, out, hu_save); break;
+        case 3: run_item<EPI, 3>(lds, it, wave, lane, K, N, out, hu_save); break;
+        case 2: run_item<EPI, 2>(lds, it, wave, lane, K, N, out, hu_save); break;
+        default: run_item<EPI, 1>(lds, it, wave, lane, K, N, out, hu_save); break;
         }
     }
 }
