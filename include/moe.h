@@ -126,6 +126,7 @@ moe_status_t moe_route(const void *x, const void *w_router, int64_t T, int64_t d
  * cap_rows_per_dst >= (T/n_src) * n_src * min(k, E/n_dst) (the tight form of the
  * article's bound: a token sends at most min(k, E/N) rows to one destination).
  * Tokens must list k distinct experts in [0, E); violations raise the device flag.
+ * Limits: E <= 1024, k <= 32.
  * ws: at least moe_dispatch_workspace_size() bytes, 256-byte aligned; its first
  * bytes hold the device status flag that moe_dispatch_status() reads. */
 size_t moe_dispatch_workspace_size(int64_t T, int32_t E, int32_t k, const moe_layout_t *layout);

@@ -281,3 +281,23 @@ def test_split_ffn_calls_match_composite(gpu_lib):
         a, b = ref["expert_off"][e], ref["expert_off"][e + 1]
         h_ref = x_disp[a:b] @ w13[e, :F].T
         assert oracle.normwise_rel_err(_np(hu[a:b, :F]), h_ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("n_src,n_dst,Ts,E,k", [(4, 8, 600, 64, 6), (3, 1, 1000, 16, 4),
+                                                (1, 4, 2000, 384, 8), (64, 16, 16, 64, 2)])
+def test_dispatch_ep_layout_multiblock(gpu_lib, n_src, n_dst, Ts, E, k):
+    """Rank-major layouts with several 256-token plan blocks per source."""
+    moe = gpu_lib
+    T = n_src * Ts
+    g = torch.Generator().manual_seed(T + E)
+    idx = torch.stack([torch.randperm(E, generator=g)[:k] for _ in range(T)]).to(torch.int32)
+    cap = n_src * Ts * max(k, E // n_dst)
+    _say(f"ep multiblock n_src={n_src} n_dst={n_dst} Ts={Ts} E={E} k={k}")
+    x = torch.randn((T, 64), generator=g).to(torch.bfloat16).cuda()
+    out = moe.moe_dispatch(x, idx.cuda(), E, layout=moe.Layout(n_src, n_dst, cap))
+    assert moe.moe_dispatch_status(out["ws"]) == 0
+    ref = oracle.plan(idx.numpy(), E, n_src, n_dst, cap)
+    _check_plan(out, ref)
+    rp = out["row_pair"]
+    live = torch.nonzero(rp >= 0).squeeze(1)
+    assert torch.equal(out["x_disp"][live].view(torch.int16), x[(rp[live] // k).long()].view(torch.int16))

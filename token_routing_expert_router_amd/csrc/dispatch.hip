@@ -15,12 +15,12 @@
 //                 block's per-expert counts.
 //   k_plan_scan   one workgroup: per-source counts, expert offsets, chunk offsets
 //                 per destination, and the first row of every (block, expert).
-//   k_plan_slots  rebuilds the masks; a pair's rank inside its expert is the
+//   k_plan_slots_copy  rebuilds the masks; a pair's rank inside its expert is the
 //                 popcount of the mask bits below its token, so tokens keep their
-//                 order inside every expert.
-//   k_row_fill    marks rows no pair uses with -1 in row_pair.
-// Copy kernel: one wavefront per token reads the row once with 16-byte loads and
-// writes it to each of its k rows (coalesced 1 KiB per wavefront instruction).
+//                 order inside every expert; marks unused rows with -1; then copies:
+//                 one wavefront per token reads the row once with 16-byte loads and
+//                 writes it to each of its k rows (1 KiB per wavefront instruction).
+// Prefix sums in k_plan_scan are segmented scans built from wavefront shuffles.
 #include "common.h"
 
 namespace moe {
@@ -29,7 +29,7 @@ namespace {
 constexpr int kPlanBlock = 256;                 // tokens per plan block
 constexpr int kMaskWords = kPlanBlock / 64;     // 64-bit words per expert mask
 constexpr int kScanThreads = 1024;
-constexpr int kScanLdsInts = 16384;             // 64 KiB of LDS for the scan
+constexpr int kScanLdsInts = 32768;             // 128 KiB of LDS for the scan
 
 struct PlanGeom {
     int T, k, E, n_src, n_dst, Ts, bps, B, epr;
@@ -96,154 +96,210 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_count(const int *__restrict
     }
 }
 
+// Block-wide exclusive scan of a[0..n) in LDS, restarting at every multiple of L
+// (segments of length L). Each thread scans a contiguous chunk serially; the chunk
+// aggregates (segment-start flag, sum) are combined by a segmented scan with
+// wavefront shuffles, then across the 16 wavefronts through LDS; the carry is added
+// to the chunk's elements before its first segment start. seg_total[s] (if
+// non-null) receives the sum of segment s. Two barriers, whatever n is.
+__device__ void seg_exclusive_scan(int *a, int n, int L, int *seg_total, int *wf_flag,
+                                   int *wf_sum /* [kScanThreads / 64] each */) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int per = (n + kScanThreads - 1) / kScanThreads;
+    const int lo = min(n, tid * per), hi = min(n, lo + per);
+    int run = 0, flag = 0;
+    for (int i = lo; i < hi; ++i) {
+        if (i % L == 0) {
+            run = 0;
+            flag = 1;
+        }
+        const int v = a[i];
+        a[i] = run;
+        run += v;
+        if (i % L == L - 1 && seg_total) seg_total[i / L] = v;   // keep the last value
+    }
+    // inclusive segmented scan over the lanes of this wavefront
+    int f = flag, v = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int of = __shfl_up(f, off, 64), ov = __shfl_up(v, off, 64);
+        if (lane >= off && !f) {
+            v += ov;
+            f = of;
+        }
+    }
+    if (lane == 63) {
+        wf_flag[wave] = f;
+        wf_sum[wave] = v;
+    }
+    __syncthreads();
+    // carry from the wavefronts before this one
+    int cf = 0, cv = 0;
+    for (int w = 0; w < wave; ++w) {
+        if (wf_flag[w]) {
+            cf = 1;
+            cv = wf_sum[w];
+        } else {
+            cv += wf_sum[w];
+        }
+    }
+    if (!f) v += cv;                     // this lane's inclusive value, carry included
+    int prev = __shfl_up(v, 1, 64);      // exclusive carry into this chunk
+    if (lane == 0) prev = cv;
+    (void)cf;
+    for (int i = lo; i < hi; ++i) {
+        if (i % L == 0) break;
+        a[i] += prev;
+    }
+    __syncthreads();
+    if (seg_total) {
+        for (int sg = tid; sg < n / L; sg += kScanThreads) seg_total[sg] += a[sg * L + L - 1];
+        __syncthreads();
+    }
+}
+
+// One workgroup, everything in LDS:
+//   bct [ns][E][bps]  block counts, then their prefix over the source's blocks
+//   cnt [ns][E]       per-source counts, then rows before e inside its chunk
+//   tot [E+1]         per-expert totals, then expert_off
+//   chk [nd][ns+1]    chunk sizes (sender order), then chunk offsets
 __global__ __launch_bounds__(kScanThreads) void k_plan_scan(
     const int *__restrict__ blk_counts, const int *__restrict__ blk_flags, PlanGeom g,
     int *__restrict__ counts, int *__restrict__ expert_off, int *__restrict__ chunk_off,
     int *__restrict__ blk_base, int *__restrict__ flag) {
     extern __shared__ int lds[];
     __shared__ int sflag;
-    const int E = g.E, ns = g.n_src, nd = g.n_dst, epr = g.epr;
-    int *cnt = lds;                      // [ns][E]: counts, then rows before e in its chunk
-    int *tot = cnt + ns * E;             // [E]: per-expert totals, then their scan
-    int *chk = tot + E;                  // [ns][nd]: chunk sizes, then chunk offsets
+    __shared__ int tf[kScanThreads / 64], ts[kScanThreads / 64];
+    const int E = g.E, ns = g.n_src, nd = g.n_dst, epr = g.epr, bps = g.bps;
+    int *bct = lds;
+    int *cnt = bct + ns * E * bps;
+    int *tot = cnt + ns * E;
+    int *chk = tot + E + 1;
+    int *segt = chk + nd * (ns + 1);            // [ns * nd] chunk sizes
     const int tid = threadIdx.x;
     if (tid == 0) sflag = 0;
     __syncthreads();
     for (int b = tid; b < g.B; b += kScanThreads)
         if (blk_flags[b]) atomicOr(&sflag, blk_flags[b]);
-
-    // per-source counts
+    // block counts, transposed so that one (source, expert)'s blocks are contiguous
+    for (int i = tid; i < g.B * E; i += kScanThreads) {
+        const int b = i / E, e = i % E;
+        const int s = b / bps, bb = b % bps;
+        bct[(s * E + e) * bps + bb] = blk_counts[i];
+    }
+    __syncthreads();
+    // per-source counts, prefix over each source's blocks
     for (int se = tid; se < ns * E; se += kScanThreads) {
-        const int s = se / E, e = se % E;
         int c = 0;
-        for (int bb = 0; bb < g.bps; ++bb) c += blk_counts[size_t(s * g.bps + bb) * E + e];
+        for (int bb = 0; bb < bps; ++bb) c += bct[se * bps + bb];
         cnt[se] = c;
         counts[se] = c;
     }
     __syncthreads();
-    // per-expert totals
+    seg_exclusive_scan(bct, ns * E * bps, bps, nullptr, tf, ts);
     for (int e = tid; e < E; e += kScanThreads) {
         int c = 0;
         for (int s = 0; s < ns; ++s) c += cnt[s * E + e];
         tot[e] = c;
     }
     __syncthreads();
-    // rows before expert e inside (source s -> destination r), and chunk sizes
-    for (int sr = tid; sr < ns * nd; sr += kScanThreads) {
-        const int s = sr / nd, r = sr % nd;
-        int run = 0;
-        for (int e = r * epr; e < (r + 1) * epr; ++e) {
-            const int c = cnt[s * E + e];
-            cnt[s * E + e] = run;
-            run += c;
-        }
-        chk[s * nd + r] = run;
+    // rows before expert e inside (source s -> its destination); chunk sizes
+    seg_exclusive_scan(cnt, ns * E, epr, segt, tf, ts);
+    // chunk offsets of every destination in sender order: chk[r][s]
+    for (int i = tid; i < nd * ns; i += kScanThreads) {
+        const int r = i / ns, s = i % ns;
+        chk[r * (ns + 1) + s] = segt[s * nd + r];
     }
     __syncthreads();
-    // chunk offsets inside every destination, in sender order
-    for (int r = tid; r < nd; r += kScanThreads) {
-        int run = 0;
-        for (int s = 0; s < ns; ++s) {
-            const int c = chk[s * nd + r];
-            chk[s * nd + r] = run;
-            chunk_off[r * (ns + 1) + s] = run;
-            run += c;
-        }
-        chunk_off[r * (ns + 1) + ns] = run;
-        if (int64_t(run) > g.cap) atomicOr(&sflag, kFlagCapacity);
+    for (int r = tid; r < nd; r += kScanThreads) chk[r * (ns + 1) + ns] = 0;
+    __syncthreads();
+    seg_exclusive_scan(chk, nd * (ns + 1), ns + 1, nullptr, tf, ts);
+    for (int i = tid; i < nd * (ns + 1); i += kScanThreads) {
+        chunk_off[i] = chk[i];
+        if (i % (ns + 1) == ns && int64_t(chk[i]) > g.cap) atomicOr(&sflag, kFlagCapacity);
     }
-    // exclusive scan of the per-expert totals (E <= 1024: one value per thread)
-    {
-        int v = (tid < E) ? tot[tid] : 0;
-        const int own = v;
-        __syncthreads();
-        for (int off = 1; off < kScanThreads; off <<= 1) {
-            if (tid < E) tot[tid] = v;
-            __syncthreads();
-            if (tid >= off && tid < E) v += tot[tid - off];
-            __syncthreads();
-        }
-        if (tid < E) expert_off[tid] = v - own;
-        if (tid == E - 1) expert_off[E] = v;
-    }
+    // expert offsets
+    tot[E] = 0;
+    __syncthreads();
+    seg_exclusive_scan(tot, E + 1, E + 1, nullptr, tf, ts);
+    for (int e = tid; e <= E; e += kScanThreads) expert_off[e] = tot[e];
     __syncthreads();
     if (tid == 0) *flag = sflag;      // overwrites the previous call's flag
     // first row of every (block, expert)
-    for (int se = tid; se < ns * E; se += kScanThreads) {
-        const int s = se / E, e = se % E, r = e / epr;
-        int run = int(int64_t(r) * g.cap) + chk[s * nd + r] + cnt[se];
-        for (int bb = 0; bb < g.bps; ++bb) {
-            const size_t b = size_t(s * g.bps + bb) * E + e;
-            blk_base[b] = run;
-            run += blk_counts[b];
-        }
+    for (int i = tid; i < g.B * E; i += kScanThreads) {
+        const int b = i / E, e = i % E;
+        const int s = b / bps, bb = b % bps, r = e / epr;
+        blk_base[i] = int(int64_t(r) * g.cap) + chk[r * (ns + 1) + s] + cnt[s * E + e] +
+                      bct[(s * E + e) * bps + bb];
     }
 }
 
-__global__ __launch_bounds__(kPlanBlock) void k_plan_slots(const int *__restrict__ idx, PlanGeom g,
-                                                          const int *__restrict__ blk_base,
-                                                          int *__restrict__ pair_slot,
-                                                          int *__restrict__ row_pair,
-                                                          int *__restrict__ flag) {
+// Slots, unused-row marking and the copy, fused. Workgroup (b, q) rebuilds the masks
+// of plan block b, assigns the slots of its kSubTokens tokens (pair_slot, row_pair),
+// then copies those tokens: one wavefront per token reads the row once with 16-byte
+// loads and writes it to each of its k rows. All workgroups together also mark the
+// rows no pair uses with row_pair = -1.
+constexpr int kSubTokens = 32;
+constexpr int kSubPerBlock = kPlanBlock / kSubTokens;
+
+__global__ __launch_bounds__(kPlanBlock) void k_plan_slots_copy(
+    const int *__restrict__ idx, PlanGeom g, const int *__restrict__ blk_base,
+    const int *__restrict__ chunk_off, int *__restrict__ pair_slot, int *__restrict__ row_pair,
+    int *__restrict__ flag, const uint4 *__restrict__ x, int rc, uint4 *__restrict__ x_disp) {
     extern __shared__ unsigned long long masks[];
-    const int b = blockIdx.x;
+    __shared__ int sl[kSubTokens][32];
+    const int b = blockIdx.x / kSubPerBlock, q = blockIdx.x % kSubPerBlock;
     const int s = b / g.bps, tb = (b % g.bps) * kPlanBlock;
     const int n = min(kPlanBlock, g.Ts - tb);
     const int t_begin = s * g.Ts + tb;
-    build_masks(masks, idx, t_begin, n, g.k, g.E, flag);
+    const int64_t rows_total = int64_t(g.n_dst) * g.cap;
+    build_masks(masks, idx, t_begin, n, g.k, g.E, flag);   // every workgroup of block b
     const int t = threadIdx.x;
-    if (t >= n) return;
-    const int tg = t_begin + t;
-    for (int j = 0; j < g.k; ++j) {
-        const int e = idx[size_t(tg) * g.k + j];
-        int slot = -1;
-        if (e >= 0 && e < g.E) {
-            const unsigned long long *m = masks + e * kMaskWords;
-            int rank = 0;
-            for (int w = 0; w < (t >> 6); ++w) rank += __popcll(m[w]);
-            rank += __popcll(m[t >> 6] & ((1ull << (t & 63)) - 1ull));
-            const int row = blk_base[size_t(b) * g.E + e] + rank;
-            const int r = e / g.epr;
-            if (int64_t(row) - int64_t(r) * g.cap < g.cap) {
-                slot = row;
-                row_pair[row] = tg * g.k + j;
-            } else {
-                atomicOr(flag, kFlagCapacity);
+    if (t >= q * kSubTokens && t < (q + 1) * kSubTokens && t < n) {
+        const int tg = t_begin + t;
+        for (int j = 0; j < g.k; ++j) {
+            const int e = idx[size_t(tg) * g.k + j];
+            int slot = -1;
+            if (e >= 0 && e < g.E) {
+                const unsigned long long *m = masks + e * kMaskWords;
+                int rank = 0;
+                for (int w = 0; w < (t >> 6); ++w) rank += __popcll(m[w]);
+                rank += __popcll(m[t >> 6] & ((1ull << (t & 63)) - 1ull));
+                const int row = blk_base[size_t(b) * g.E + e] + rank;
+                const int r = e / g.epr;
+                if (int64_t(row) - int64_t(r) * g.cap < g.cap) {
+                    slot = row;
+                    row_pair[row] = tg * g.k + j;
+                } else {
+                    atomicOr(flag, kFlagCapacity);
+                }
             }
+            pair_slot[size_t(tg) * g.k + j] = slot;
+            sl[t - q * kSubTokens][j] = slot;
         }
-        pair_slot[size_t(tg) * g.k + j] = slot;
     }
-}
-
-__global__ void k_row_fill(PlanGeom g, const int *__restrict__ chunk_off, int *__restrict__ row_pair) {
-    const int64_t total = int64_t(g.n_dst) * g.cap;
-    for (int64_t row = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; row < total;
+    // rows that no pair uses
+    for (int64_t row = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; row < rows_total;
          row += int64_t(gridDim.x) * blockDim.x) {
         const int r = int(row / g.cap);
-        const int64_t in_r = row - int64_t(r) * g.cap;
-        if (in_r >= chunk_off[r * (g.n_src + 1) + g.n_src]) row_pair[row] = -1;
+        if (row - int64_t(r) * g.cap >= chunk_off[r * (g.n_src + 1) + g.n_src]) row_pair[row] = -1;
     }
-}
-
-// x_disp[pair_slot[t,j]] = x[t]: one wavefront per token, 16-byte chunks.
-__global__ __launch_bounds__(256) void k_dispatch_rows(const uint4 *__restrict__ x,
-                                                       const int *__restrict__ pair_slot, int T,
-                                                       int k, int rc, int64_t rows_total,
-                                                       uint4 *__restrict__ x_disp) {
+    if (x == nullptr) return;
+    __syncthreads();
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave0 = __builtin_amdgcn_readfirstlane((blockIdx.x * blockDim.x + threadIdx.x) / kWave);
-    const int nwaves = gridDim.x * blockDim.x / kWave;
-    for (int t = wave0; t < T; t += nwaves) {
-        const int *ps = pair_slot + size_t(t) * k;
-        const uint4 *src = x + size_t(t) * rc;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int tcount = min(kSubTokens, n - q * kSubTokens);
+    for (int i = wave; i < tcount; i += kPlanBlock / kWave) {
+        const uint4 *src = x + size_t(t_begin + q * kSubTokens + i) * rc;
         int c = lane;
         for (; c + 3 * kWave < rc; c += 4 * kWave) {
             const uint4 v0 = src[c], v1 = src[c + kWave], v2 = src[c + 2 * kWave],
                         v3 = src[c + 3 * kWave];
-            for (int j = 0; j < k; ++j) {
-                const int s = ps[j];
-                if (s < 0 || s >= rows_total) continue;
-                uint4 *dst = x_disp + size_t(s) * rc;
+            for (int j = 0; j < g.k; ++j) {
+                const int sj = sl[i][j];
+                if (sj < 0 || sj >= rows_total) continue;
+                uint4 *dst = x_disp + size_t(sj) * rc;
                 dst[c] = v0;
                 dst[c + kWave] = v1;
                 dst[c + 2 * kWave] = v2;
@@ -252,10 +308,10 @@ __global__ __launch_bounds__(256) void k_dispatch_rows(const uint4 *__restrict__
         }
         for (; c < rc; c += kWave) {
             const uint4 v = src[c];
-            for (int j = 0; j < k; ++j) {
-                const int s = ps[j];
-                if (s < 0 || s >= rows_total) continue;
-                x_disp[size_t(s) * rc + c] = v;
+            for (int j = 0; j < g.k; ++j) {
+                const int sj = sl[i][j];
+                if (sj < 0 || sj >= rows_total) continue;
+                x_disp[size_t(sj) * rc + c] = v;
             }
         }
     }
@@ -304,6 +360,15 @@ __global__ __launch_bounds__(256) void k_dispatch_bwd(const uint4 *__restrict__ 
     }
 }
 
+bool set_scan_lds_limit() {
+    static int ok = -1;
+    if (ok < 0)
+        ok = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_plan_scan),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 kScanLdsInts * int(sizeof(int))) == hipSuccess;
+    return ok == 1;
+}
+
 int copy_grid(int64_t T) { return int(std::min<int64_t>(cdiv(T, 4), 8192)); }
 
 }  // namespace
@@ -330,14 +395,16 @@ extern "C" moe_status_t moe_dispatch(const void *x, const int32_t *topk_idx, int
         return MOE_ERR_INVALID_ARG;
     const int n_src = layout ? layout->n_src : 1, n_dst = layout ? layout->n_dst : 1;
     if (T % n_src != 0 || E % n_dst != 0) return MOE_ERR_SHAPE;
-    if (E > 1024 || T * k >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+    if (E > 1024 || k > 32 || T * k >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
     const PlanGeom g = make_geom(T, E, k, layout);
     // tight form of the receive bound: a token sends at most min(k, E/N) rows to one
     // destination, so a destination receives at most n_src * Ts * min(k, E/N) rows
     const int64_t need = int64_t(n_src) * g.Ts * std::min<int64_t>(k, g.epr);
     if (g.cap < need) return MOE_ERR_CAPACITY;
     if (int64_t(n_dst) * g.cap >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
-    const size_t lds_scan = size_t(n_src * E + E + n_src * n_dst) * sizeof(int);
+    const size_t lds_scan = size_t(int64_t(g.B) * E + int64_t(n_src) * E + E + 1 +
+                                   int64_t(n_dst) * (n_src + 1) + int64_t(n_src) * n_dst) *
+                            sizeof(int);
     if (lds_scan > size_t(kScanLdsInts) * sizeof(int)) return MOE_ERR_UNSUPPORTED;
     if (T == 0) return MOE_OK;
     if (!topk_idx || !counts || !expert_off || !chunk_off || !pair_slot || !row_pair || !ws)
@@ -348,6 +415,7 @@ extern "C" moe_status_t moe_dispatch(const void *x, const int32_t *topk_idx, int
     const int64_t rowb = d * elt_size(dtype);
     if (x && (rowb % 16 != 0 || !aligned16(x) || !aligned16(x_disp))) return MOE_ERR_ALIGN;
 
+    if (!set_scan_lds_limit()) return MOE_ERR_HIP;   // first HIP call: all checks done
     const hipStream_t st = as_stream(stream);
     char *wsb = static_cast<char *>(ws);
     int *flag = reinterpret_cast<int *>(wsb);
@@ -360,18 +428,9 @@ extern "C" moe_status_t moe_dispatch(const void *x, const int32_t *topk_idx, int
                        blk_counts, blk_flags);
     hipLaunchKernelGGL(k_plan_scan, dim3(1), dim3(kScanThreads), lds_scan, st, blk_counts,
                        blk_flags, g, counts, expert_off, chunk_off, blk_base, flag);
-    hipLaunchKernelGGL(k_plan_slots, dim3(g.B), dim3(kPlanBlock), lds_mask, st, topk_idx, g,
-                       blk_base, pair_slot, row_pair, flag);
-    {
-        const int64_t rows = int64_t(n_dst) * g.cap;
-        const int grid = int(std::min<int64_t>(cdiv(rows, 256), 4096));
-        hipLaunchKernelGGL(k_row_fill, dim3(grid), dim3(256), 0, st, g, chunk_off, row_pair);
-    }
-    if (x) {
-        hipLaunchKernelGGL(k_dispatch_rows, dim3(copy_grid(T)), dim3(256), 0, st,
-                           static_cast<const uint4 *>(x), pair_slot, int(T), k, int(rowb / 16),
-                           int64_t(n_dst) * g.cap, static_cast<uint4 *>(x_disp));
-    }
+    hipLaunchKernelGGL(k_plan_slots_copy, dim3(g.B * kSubPerBlock), dim3(kPlanBlock), lds_mask, st,
+                       topk_idx, g, blk_base, chunk_off, pair_slot, row_pair, flag,
+                       static_cast<const uint4 *>(x), int(rowb / 16), static_cast<uint4 *>(x_disp));
     return launch_status();
 }
 

@@ -17,6 +17,8 @@ namespace {
 constexpr int kRouteBK = 32;      // input elements per LDS stage
 constexpr int kRouteThreads = 256;
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 template <int DT, int TM, int TE>
 __global__ __launch_bounds__(kRouteThreads) void k_router_topk(
     const void *__restrict__ xv, const void *__restrict__ wv, int T, int d, int E, int k,
@@ -31,6 +33,8 @@ __global__ __launch_bounds__(kRouteThreads) void k_router_topk(
     constexpr int VN = Vec<DT>::N;        // elements per 16-byte chunk
     constexpr int CH = BK / VN;           // chunks per tile row
     constexpr int NV = (EP + kWave - 1) / kWave;
+    constexpr int NXC = (TT * CH + kRouteThreads - 1) / kRouteThreads;   // x chunks per thread
+    constexpr int NWC = (EP * CH + kRouteThreads - 1) / kRouteThreads;   // w chunks per thread
     static_assert(TT * SL <= BK * SW, "logits tile must fit in the w staging area");
     static_assert(NV <= 32, "experts per lane");
 
@@ -41,7 +45,8 @@ __global__ __launch_bounds__(kRouteThreads) void k_router_topk(
     const int eg = tid & 31;              // expert group: experts eg, eg+32, ...
     const int tg = tid >> 5;              // token group: tokens tg*TM .. tg*TM+TM-1
     const int t0 = blockIdx.x * TT;
-    const size_t rowb = size_t(d) * (DT == MOE_BF16 ? 2 : 4);   // bytes per row
+    const int esz = (DT == MOE_BF16) ? 2 : 4;
+    const size_t rowb = size_t(d) * esz;
     const char *xb = static_cast<const char *>(xv);
     const char *wb = static_cast<const char *>(wv);
 
@@ -51,40 +56,59 @@ __global__ __launch_bounds__(kRouteThreads) void k_router_topk(
 #pragma unroll
         for (int q = 0; q < TE; ++q) acc[m][q] = 0.0f;
 
+    // Next stage's chunks are fetched into registers while the current stage is
+    // consumed from LDS (elements past T, E or d read as zero; they never reach an
+    // output: padded experts and tokens are dropped, and the last stage stops at d).
+    u32x4 rx[NXC], rw[NWC];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int j = 0; j < NXC; ++j) {
+            const int c = tid + j * kRouteThreads;
+            const int r = c / CH, kk = k0 + (c % CH) * VN;
+            rx[j] = (c < TT * CH && t0 + r < T && kk < d)
+                        ? *reinterpret_cast<const u32x4 *>(xb + size_t(t0 + r) * rowb + size_t(kk) * esz)
+                        : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int j = 0; j < NWC; ++j) {
+            const int c = tid + j * kRouteThreads;
+            const int e = c / CH, kk = k0 + (c % CH) * VN;
+            rw[j] = (c < EP * CH && e < E && kk < d)
+                        ? *reinterpret_cast<const u32x4 *>(wb + size_t(e) * rowb + size_t(kk) * esz)
+                        : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto stage = [&]() {
+#pragma unroll
+        for (int j = 0; j < NXC; ++j) {
+            const int c = tid + j * kRouteThreads;
+            if (c < TT * CH) {
+                const int r = c / CH, kc = c % CH;
+                float f[VN];
+                Vec<DT>::unpack(make_uint4(rx[j].x, rx[j].y, rx[j].z, rx[j].w), f);
+#pragma unroll
+                for (int i = 0; i < VN; ++i) xs[(kc * VN + i) * SX + r] = f[i];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NWC; ++j) {
+            const int c = tid + j * kRouteThreads;
+            if (c < EP * CH) {
+                const int e = c / CH, kc = c % CH;
+                float f[VN];
+                Vec<DT>::unpack(make_uint4(rw[j].x, rw[j].y, rw[j].z, rw[j].w), f);
+#pragma unroll
+                for (int i = 0; i < VN; ++i) wsm[(kc * VN + i) * SW + e] = f[i];
+            }
+        }
+    };
+
+    fetch(0);
+    stage();
+    __syncthreads();
     for (int k0 = 0; k0 < d; k0 += BK) {
-        // stage x[t0:t0+TT, k0:k0+BK] and w[:, k0:k0+BK] as float32, k-major
-        // (zeros past T, E or d; padded experts and tokens are never output).
-        for (int c = tid; c < TT * CH; c += kRouteThreads) {
-            const int r = c / CH, kc = c % CH;
-            const int t = t0 + r, kk = k0 + kc * VN;
-            float f[VN];
-            if (t < T && kk < d) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(xb + size_t(t) * rowb +
-                                                                 size_t(kk) * (DT == MOE_BF16 ? 2 : 4));
-                Vec<DT>::unpack(v, f);
-            } else {
-#pragma unroll
-                for (int i = 0; i < VN; ++i) f[i] = 0.0f;
-            }
-#pragma unroll
-            for (int i = 0; i < VN; ++i) xs[(kc * VN + i) * SX + r] = f[i];
-        }
-        for (int c = tid; c < EP * CH; c += kRouteThreads) {
-            const int e = c / CH, kc = c % CH;
-            const int kk = k0 + kc * VN;
-            float f[VN];
-            if (e < E && kk < d) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(wb + size_t(e) * rowb +
-                                                                 size_t(kk) * (DT == MOE_BF16 ? 2 : 4));
-                Vec<DT>::unpack(v, f);
-            } else {
-#pragma unroll
-                for (int i = 0; i < VN; ++i) f[i] = 0.0f;
-            }
-#pragma unroll
-            for (int i = 0; i < VN; ++i) wsm[(kc * VN + i) * SW + e] = f[i];
-        }
-        __syncthreads();
+        const bool more = k0 + BK < d;
+        if (more) fetch(k0 + BK);
         auto step = [&](int kk) {
             float xr[TM], wr[TE];
 #pragma unroll
@@ -97,13 +121,17 @@ __global__ __launch_bounds__(kRouteThreads) void k_router_topk(
                 for (int q = 0; q < TE; ++q) acc[m][q] = __builtin_fmaf(xr[m], wr[q], acc[m][q]);
         };
         if (k0 + BK <= d) {
-#pragma unroll 4
+#pragma unroll 8
             for (int kk = 0; kk < BK; ++kk) step(kk);
         } else {
             // last, partial stage: the chain stops exactly at i = d-1
             for (int kk = 0; kk < d - k0; ++kk) step(kk);
         }
         __syncthreads();
+        if (more) {
+            stage();
+            __syncthreads();
+        }
     }
 
     // logits tile -> LDS (reusing the w staging area)
