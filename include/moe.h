@@ -188,13 +188,16 @@ moe_status_t moe_combine(const void *y_disp, const int32_t *pair_slot, const flo
  *
  * moe_combine_bwd:  dy_disp[pair_slot[t,j]] = topk_w[t,j] * dy[t]      (dtype)
  *                   dtopk_w[t,j] = <dy[t], y_disp[pair_slot[t,j]]>    (f32)
- * moe_expert_ffn_bwd, per expert e with X, dO = dy_disp rows of e, h, u from hu_save:
+ * moe_expert_ffn_bwd (bf16 only), per expert e with X, dO = dy_disp rows of e, h, u
+ * from hu_save (written by moe_expert_ffn):
  *                   dA = dO W2;  dh = dA * u * s * (1 + h (1 - s)), s = sigmoid(h);
  *                   du = dA * silu(h);  dX = dh W1 + du W3      -> dx_disp (dtype)
  *                   dW2 = dO^T a;  dW1 = dh^T X;  dW3 = du^T X  -> dw2, dw13 (f32)
- * moe_route_bwd:    dlogits_sel[t,j] = g_j (dg_j - sum_i g_i dg_i)   (f32, RENORM)
- *                   dw_router[e,:] = sum over pairs (t,j) with idx e of
- *                                    dlogits_sel[t,j] * x[t,:]        (f32)
+ * moe_route_bwd:    dlogits_sel[t,j] = g_j (dg_j - sum_i g_i dg_i)   (f32, RENORM gating)
+ *                   dw_router[e,:] = sum over the rows of expert e in the expert-major
+ *                                    plan (expert_off, row_pair from moe_dispatch),
+ *                                    i.e. its tokens in ascending order, of
+ *                                    dlogits_sel[t,j] * x[t,:]      (f32)
  * moe_dispatch_bwd: dx[t] = sum_j dx_disp[pair_slot[t,j]]
  *                           + sum_j dlogits_sel[t,j] * w_router[topk_idx[t,j]]
  *                   (second term skipped if dlogits_sel is NULL), float32 sum in
@@ -211,11 +214,10 @@ moe_status_t moe_expert_ffn_bwd(const void *x_disp, const void *dy_disp, const v
                                 int32_t E, int64_t rows, int64_t d, int64_t F,
                                 moe_dtype_t dtype, void *dx_disp, float *dw13, float *dw2,
                                 void *ws, size_t ws_bytes, void *stream);
-size_t moe_route_bwd_workspace_size(int64_t T, int64_t d, int32_t E, int32_t k);
 moe_status_t moe_route_bwd(const void *x, const int32_t *topk_idx, const float *topk_w,
-                           const float *dtopk_w, int64_t T, int64_t d, int32_t E, int32_t k,
-                           moe_dtype_t dtype, float *dlogits_sel, float *dw_router, void *ws,
-                           size_t ws_bytes, void *stream);
+                           const float *dtopk_w, const int32_t *expert_off,
+                           const int32_t *row_pair, int64_t T, int64_t d, int32_t E, int32_t k,
+                           moe_dtype_t dtype, float *dlogits_sel, float *dw_router, void *stream);
 moe_status_t moe_dispatch_bwd(const void *dx_disp, const int32_t *pair_slot,
                               const int32_t *topk_idx, const float *dlogits_sel,
                               const void *w_router, int64_t T, int32_t k, int64_t d, int32_t E,

@@ -21,6 +21,7 @@ __all__ = ["MoEError", "load", "library_path", "moe_abi_version", "moe_route", "
            "moe_dispatch_status", "moe_expert_ffn", "moe_expert_ffn_gate_up",
            "moe_expert_ffn_down", "moe_combine", "moe_combine_bwd",
            "moe_expert_ffn_bwd", "moe_route_bwd", "moe_dispatch_bwd", "Layout", "forward",
+           "backward",
            "EXPORTED"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -53,8 +54,7 @@ EXPORTED = {
     "moe_expert_ffn_bwd_workspace_size": (_SZ, [_I32, _I64, _I64, _I64, _I32]),
     "moe_expert_ffn_bwd": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I32, _P, _P,
                                   _P, _P, _SZ, _P]),
-    "moe_route_bwd_workspace_size": (_SZ, [_I64, _I64, _I32, _I32]),
-    "moe_route_bwd": (_I32, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _SZ, _P]),
+    "moe_route_bwd": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _P, _P, _P]),
     "moe_dispatch_bwd": (_I32, [_P, _P, _P, _P, _P, _I64, _I32, _I64, _I32, _I64, _I32, _P,
                                 _P]),
 }
@@ -276,21 +276,17 @@ def moe_expert_ffn_bwd(x_disp, dy_disp, hu_save, expert_off, w13, w2, *, dx_disp
     return dx_disp, dw13, dw2
 
 
-def moe_route_bwd(x, topk_idx, topk_w, dtopk_w, E: int, *, dlogits_sel=None, dw_router=None,
-                  ws=None, stream=None):
+def moe_route_bwd(x, topk_idx, topk_w, dtopk_w, expert_off, row_pair, E: int, *,
+                  dlogits_sel=None, dw_router=None, stream=None):
     T, d = x.shape
     k = topk_idx.shape[1]
-    lib = load()
-    need = int(lib.moe_route_bwd_workspace_size(T, d, E, k))
-    if ws is None:
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
     if dlogits_sel is None:
         dlogits_sel = torch.empty((T, k), dtype=torch.float32, device=x.device)
     if dw_router is None:
         dw_router = torch.empty((E, d), dtype=torch.float32, device=x.device)
-    _check("moe_route_bwd", lib.moe_route_bwd(
-        _ptr(x), _ptr(topk_idx), _ptr(topk_w), _ptr(dtopk_w), T, d, E, k, _dt(x),
-        _ptr(dlogits_sel), _ptr(dw_router), _ptr(ws), ws.numel(), _stream(stream)))
+    _check("moe_route_bwd", load().moe_route_bwd(
+        _ptr(x), _ptr(topk_idx), _ptr(topk_w), _ptr(dtopk_w), _ptr(expert_off), _ptr(row_pair),
+        T, d, E, k, _dt(x), _ptr(dlogits_sel), _ptr(dw_router), _stream(stream)))
     return dlogits_sel, dw_router
 
 
@@ -308,6 +304,24 @@ def moe_dispatch_bwd(dx_disp, pair_slot, *, topk_idx=None, dlogits_sel=None, w_r
 
 
 # ------------------------------------------------------------ whole layer
+def backward(x, w_router, w13, w2, fwd: dict, dy, *, stream=None):
+    """Gradients of sum(dy * y) for a forward() run with save_for_backward=True:
+    combine_bwd -> expert_ffn_bwd -> route_bwd -> dispatch_bwd. Returns a dict with
+    dx, dw_router, dw13, dw2 and the intermediates."""
+    E = w_router.shape[0]
+    dy_disp, dgates = moe_combine_bwd(dy, fwd["y_disp"], fwd["pair_slot"], fwd["topk_w"],
+                                      stream=stream)
+    dx_disp, dw13, dw2 = moe_expert_ffn_bwd(fwd["x_disp"], dy_disp, fwd["hu_save"],
+                                            fwd["expert_off"], w13, w2, stream=stream)
+    dl, dwr = moe_route_bwd(x, fwd["topk_idx"], fwd["topk_w"], dgates, fwd["expert_off"],
+                            fwd["row_pair"], E, stream=stream)
+    dx = moe_dispatch_bwd(dx_disp, fwd["pair_slot"], topk_idx=fwd["topk_idx"], dlogits_sel=dl,
+                          w_router=w_router, stream=stream)
+    return dict(dy_disp=dy_disp, dgates=dgates, dx_disp=dx_disp, dw13=dw13, dw2=dw2,
+                dlogits_sel=dl, dw_router=dwr, dx=dx)
+
+
+
 def forward(x, w_router, w13, w2, k: int, *, save_for_backward: bool = False, stream=None):
     """route -> dispatch -> expert FFN -> combine. Returns a dict of all outputs."""
     E = w_router.shape[0]

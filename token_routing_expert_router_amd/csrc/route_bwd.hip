@@ -1,0 +1,86 @@
+// Backward of the router: the softmax-over-top-k Jacobian and the router weights'
+// gradient. With g the k gates of a token and dg their upstream gradient,
+//   dl_j = g_j (dg_j - sum_i g_i dg_i)          (selected logits; others get none:
+//                                                the top-k choice is piecewise constant)
+//   dWr[e,:] = sum over pairs (t, j) routed to e of dl[t,j] * x[t,:]
+// The second sum runs over expert e's rows of the expert-major plan, i.e. over its
+// tokens in ascending order: one fixed order, float32 fused multiply-adds.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+__global__ void k_route_bwd_sel(const float *__restrict__ g, const float *__restrict__ dg, int T,
+                                int k, float *__restrict__ dl) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= T) return;
+    const float *gt = g + size_t(t) * k;
+    const float *dgt = dg + size_t(t) * k;
+    float s = 0.0f;
+    for (int j = 0; j < k; ++j) s = __builtin_fmaf(gt[j], dgt[j], s);
+    for (int j = 0; j < k; ++j) dl[size_t(t) * k + j] = gt[j] * (dgt[j] - s);
+}
+
+// one workgroup per (expert, 256 16-byte chunks of the row); thread = one chunk
+template <int DT>
+__global__ __launch_bounds__(256) void k_route_bwd_w(const uint4 *__restrict__ x,
+                                                     const float *__restrict__ dl,
+                                                     const int *__restrict__ expert_off,
+                                                     const int *__restrict__ row_pair, int k,
+                                                     int rc, float *__restrict__ dw) {
+    constexpr int VN = Vec<DT>::N;
+    const int e = blockIdx.x;
+    const int c = blockIdx.y * blockDim.x + threadIdx.x;
+    if (c >= rc) return;
+    const int r0 = expert_off[e], r1 = expert_off[e + 1];
+    float acc[VN];
+#pragma unroll
+    for (int i = 0; i < VN; ++i) acc[i] = 0.0f;
+    for (int r = r0; r < r1; ++r) {
+        const int p = row_pair[r];
+        if (p < 0) continue;
+        const float w = dl[p];
+        float f[VN];
+        Vec<DT>::unpack(x[size_t(p / k) * rc + c], f);
+#pragma unroll
+        for (int i = 0; i < VN; ++i) acc[i] = __builtin_fmaf(w, f[i], acc[i]);
+    }
+    float4 *out = reinterpret_cast<float4 *>(dw + size_t(e) * rc * VN + size_t(c) * VN);
+#pragma unroll
+    for (int i = 0; i < VN; i += 4) out[i / 4] = make_float4(acc[i], acc[i + 1], acc[i + 2], acc[i + 3]);
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" moe_status_t moe_route_bwd(const void *x, const int32_t *topk_idx, const float *topk_w,
+                                      const float *dtopk_w, const int32_t *expert_off,
+                                      const int32_t *row_pair, int64_t T, int64_t d, int32_t E,
+                                      int32_t k, moe_dtype_t dtype, float *dlogits_sel,
+                                      float *dw_router, void *stream) {
+    if (!valid_dtype(dtype) || T < 0 || d <= 0 || E <= 0 || k <= 0) return MOE_ERR_INVALID_ARG;
+    if (k > E) return MOE_ERR_SHAPE;
+    if (E > 65535 || T * k >= (int64_t(1) << 31) || d > (int64_t(1) << 24)) return MOE_ERR_UNSUPPORTED;
+    if (!x || !topk_idx || !topk_w || !dtopk_w || !expert_off || !row_pair || !dlogits_sel ||
+        !dw_router)
+        return MOE_ERR_INVALID_ARG;
+    const int64_t rowb = d * elt_size(dtype);
+    if (rowb % 16 != 0 || !aligned16(x) || !aligned16(dw_router)) return MOE_ERR_ALIGN;
+    const hipStream_t st = as_stream(stream);
+    if (T > 0)
+        hipLaunchKernelGGL(k_route_bwd_sel, dim3(unsigned(cdiv(T, 256))), dim3(256), 0, st, topk_w,
+                           dtopk_w, int(T), k, dlogits_sel);
+    const int rc = int(rowb / 16);
+    const dim3 grid(unsigned(E), unsigned(cdiv(rc, 256)));
+    if (dtype == MOE_BF16)
+        hipLaunchKernelGGL(k_route_bwd_w<MOE_BF16>, grid, dim3(256), 0, st,
+                           static_cast<const uint4 *>(x), dlogits_sel, expert_off, row_pair, k, rc,
+                           dw_router);
+    else
+        hipLaunchKernelGGL(k_route_bwd_w<MOE_F32>, grid, dim3(256), 0, st,
+                           static_cast<const uint4 *>(x), dlogits_sel, expert_off, row_pair, k, rc,
+                           dw_router);
+    return launch_status();
+}
