@@ -1,15 +1,20 @@
 #!/usr/bin/env python3
 """Benchmark of the MoE layer's hot path on one MI355X.
 
-One step = one pass of the layer over one batch of synthetic tokens already
-resident in HBM: moe_route -> moe_dispatch -> moe_expert_ffn_gate_up ->
-moe_expert_ffn_down -> moe_combine (all libmoe HIP kernels). The default workload
-is the T=4096, d=2048, E=64, k=6, F=1408 bf16 layer forward.
+Headline step = one forward pass of the layer over one batch of synthetic tokens
+already resident in HBM: moe_route -> moe_dispatch -> moe_expert_ffn_gate_up ->
+moe_expert_ffn_down -> moe_combine (all libmoe HIP kernels), on the T=4096, d=2048,
+E=64, k=6, F=1408 bf16 layer. The same JSON line also reports:
+  train_step   forward + backward of that layer (combine_bwd, expert_ffn_bwd,
+               route_bwd, dispatch_bwd) on the same shapes,
+  ep_dispatch_combine  the rank-major dispatch and combine of 32 source ranks x 128
+               tokens, d=7168, E=384, k=8, Zipf(1.2) routing (identity experts),
+  large        the T=8192, d=7168, E=384, k=8, F=2048 layer forward (34 GB weights),
+  roofline     the dominant kernel of the headline step, timed live with HIP events,
+  cpu_baseline the CPU oracle on the host cores over whole passes of the headline
+               workload.
 
-Prints ONE JSON line: tokens/s for the whole job, per-stage times with achieved
-GB/s or TFLOP/s against MI355X peaks, the roofline of the dominant kernel (timed
-live with HIP events on the stream the kernels run on), and the CPU oracle timed
-on the host cores on a bounded sample of the same workload.
+Prints ONE JSON line.
 """
 from __future__ import annotations
 
@@ -33,17 +38,23 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mid_bf16",
-                    choices=["mid_bf16", "large_bf16", "tiny_f32"])
-    ap.add_argument("--no-cpu-baseline", action="store_true",
-                    help="skip the oracle timing (for profiler runs)")
+    ap.add_argument("--workload", default="mid_bf16", choices=["mid_bf16", "large_bf16", "tiny_f32"],
+                    help="workload of the headline forward step")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="headline only (no train step, EP dispatch/combine or large layer)")
+    ap.add_argument("--no-large", action="store_true", help="skip the 34 GB large-layer run")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--only-train", action="store_true",
+                    help="run only the forward + backward step (for profiler runs)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
 
 
 def stage_work(wl):
-    """Algorithmic bytes and flops per launch of every stage."""
+    """Algorithmic bytes and flops per launch of every forward stage."""
     b = 2 if wl.dtype == "bf16" else 4
     T, d, E, k, F = wl.T, wl.d, wl.E, wl.k, wl.F
     P = T * k
@@ -61,6 +72,23 @@ def stage_work(wl):
     }
 
 
+def bwd_work(wl):
+    b = 2
+    T, d, E, k, F = wl.T, wl.d, wl.E, wl.k, wl.F
+    P = T * k
+    return {
+        # dy read, y_disp read, dy_disp written, gate gradients written
+        "combine_bwd": dict(bytes=T * d * b + 2 * P * d * b + P * 4, flops=0, unit="hbm"),
+        # dA = dO W2 and dX = dHU W13 (weights read once each), dW2 = dO^T a and
+        # dW13 = dHU^T X (fp32 weight gradients written once); 12 P d F flops in all
+        "expert_ffn_bwd": dict(bytes=E * 3 * F * d * b + E * 3 * F * d * 4 + 2 * P * d * b
+                               + 2 * P * 2 * F * b + P * 2 * F * b + P * d * b,
+                               flops=12 * P * d * F, unit="mfma"),
+        "route_bwd": dict(bytes=P * d * b + E * d * 4, flops=2 * P * d, unit="hbm"),
+        "dispatch_bwd": dict(bytes=P * d * b + T * d * b, flops=0, unit="hbm"),
+    }
+
+
 def bound_of(work):
     """hbm or mfma/valu: whichever lower bound on the time is larger."""
     t_mem = work["bytes"] / (PEAK_HBM_GBS * 1e9)
@@ -68,7 +96,158 @@ def bound_of(work):
         return "hbm", t_mem
     peak = PEAK_BF16_TFLOPS if work["unit"] == "mfma" else PEAK_FP32_VALU_TFLOPS
     t_cmp = work["flops"] / (peak * 1e12)
+    if work["unit"] == "hbm":
+        return "hbm", t_mem
     return (work["unit"] if t_cmp >= t_mem else "hbm"), max(t_cmp, t_mem)
+
+
+def summarize(names, events, steps, work):
+    out = {}
+    for s, name in enumerate(names):
+        ms = sum(ev[s].elapsed_time(ev[s + 1]) for ev in events) / steps
+        w = work[name]
+        bound, t_lb = bound_of(w)
+        st = {"us": round(ms * 1e3, 2), "GB_s": round(w["bytes"] / (ms * 1e-3) / 1e9, 1),
+              "bound": bound, "roofline_frac": round(t_lb / (ms * 1e-3), 3)}
+        if w["flops"]:
+            st["TFLOP_s"] = round(w["flops"] / (ms * 1e-3) / 1e12, 1)
+        out[name] = st
+    return out
+
+
+def timed(torch, step, nstages, steps, warmup):
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(nstages + 1)]
+    for _ in range(warmup):
+        step(mk())
+    events = [mk() for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, events
+
+
+def forward_bench(torch, moe, wl, dev, steps, warmup):
+    import moe_synth
+    inp = moe_synth.layer_inputs(wl, device=dev)
+    x, wr, w13, w2 = inp["x"], inp["w_router"], inp["w13"], inp["w2"]
+    T, k, E, F, d = wl.T, wl.k, wl.E, wl.F, wl.d
+    # every output allocated once; the timed loop allocates nothing
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+    plan = moe.moe_dispatch(x, moe.moe_route(x, wr, k)[0], E)
+    act = torch.empty((T * k, F), dtype=x.dtype, device=dev)
+    y_disp = torch.empty((T * k, d), dtype=x.dtype, device=dev)
+    y = torch.empty((T, d), dtype=x.dtype, device=dev)
+
+    def step(ev):
+        ev[0].record()
+        moe.moe_route(x, wr, k, topk_idx=idx, topk_w=gates)
+        ev[1].record()
+        moe.moe_dispatch(x, idx, E, out=plan)
+        ev[2].record()
+        moe.moe_expert_ffn_gate_up(plan["x_disp"], plan["expert_off"], w13, act=act)
+        ev[3].record()
+        moe.moe_expert_ffn_down(act, plan["expert_off"], w2, y_disp=y_disp)
+        ev[4].record()
+        moe.moe_combine(y_disp, plan["pair_slot"], gates, y=y)
+        ev[5].record()
+
+    elapsed, events = timed(torch, step, 5, steps, warmup)
+    if moe.moe_dispatch_status(plan["ws"]) != 0:
+        raise RuntimeError("dispatch raised its device flag")
+    stages = summarize(["route", "dispatch", "gate_up", "down", "combine"], events, steps,
+                       stage_work(wl))
+    return inp, elapsed, stages
+
+
+def train_bench(torch, moe, wl, dev, steps, warmup):
+    import moe_synth
+    inp = moe_synth.layer_inputs(wl, device=dev)
+    x, wr, w13, w2 = inp["x"], inp["w_router"], inp["w13"], inp["w2"]
+    dy = moe_synth.upstream_grad(wl, device=dev)
+    T, k, E, F, d = wl.T, wl.k, wl.E, wl.F, wl.d
+    P = T * k
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+    plan = moe.moe_dispatch(x, moe.moe_route(x, wr, k)[0], E)
+    act = torch.empty((P, F), dtype=x.dtype, device=dev)
+    hu = torch.empty((P, 2 * F), dtype=x.dtype, device=dev)
+    y_disp = torch.empty((P, d), dtype=x.dtype, device=dev)
+    y = torch.empty((T, d), dtype=x.dtype, device=dev)
+    dy_disp = torch.empty((P, d), dtype=x.dtype, device=dev)
+    dgates = torch.empty((T, k), dtype=torch.float32, device=dev)
+    dx_disp = torch.empty((P, d), dtype=x.dtype, device=dev)
+    dw13 = torch.empty((E, 2 * F, d), dtype=torch.float32, device=dev)
+    dw2 = torch.empty((E, d, F), dtype=torch.float32, device=dev)
+    ws = torch.empty(int(moe.load().moe_expert_ffn_bwd_workspace_size(E, P, d, F, 1)),
+                     dtype=torch.uint8, device=dev)
+    dl = torch.empty((T, k), dtype=torch.float32, device=dev)
+    dwr = torch.empty((E, d), dtype=torch.float32, device=dev)
+    dx = torch.empty((T, d), dtype=x.dtype, device=dev)
+
+    def step(ev):
+        ev[0].record()
+        moe.moe_route(x, wr, k, topk_idx=idx, topk_w=gates)
+        moe.moe_dispatch(x, idx, E, out=plan)
+        moe.moe_expert_ffn_gate_up(plan["x_disp"], plan["expert_off"], w13, act=act, hu_save=hu)
+        moe.moe_expert_ffn_down(act, plan["expert_off"], w2, y_disp=y_disp)
+        moe.moe_combine(y_disp, plan["pair_slot"], gates, y=y)
+        ev[1].record()
+        moe.moe_combine_bwd(dy, y_disp, plan["pair_slot"], gates, dy_disp=dy_disp, dtopk_w=dgates)
+        ev[2].record()
+        moe.moe_expert_ffn_bwd(plan["x_disp"], dy_disp, hu, plan["expert_off"], w13, w2,
+                               dx_disp=dx_disp, dw13=dw13, dw2=dw2, ws=ws)
+        ev[3].record()
+        moe.moe_route_bwd(x, idx, gates, dgates, plan["expert_off"], plan["row_pair"], E,
+                          dlogits_sel=dl, dw_router=dwr)
+        ev[4].record()
+        moe.moe_dispatch_bwd(dx_disp, plan["pair_slot"], topk_idx=idx, dlogits_sel=dl,
+                             w_router=wr, dx=dx)
+        ev[5].record()
+
+    elapsed, events = timed(torch, step, 5, steps, warmup)
+    fwd_work = {"forward": dict(bytes=sum(w["bytes"] for w in stage_work(wl).values()),
+                                flops=sum(w["flops"] for w in stage_work(wl).values()), unit="mfma")}
+    fwd_work.update(bwd_work(wl))
+    stages = summarize(["forward", "combine_bwd", "expert_ffn_bwd", "route_bwd", "dispatch_bwd"],
+                       events, steps, fwd_work)
+    del inp
+    return {"workload": f"{wl.name}: forward + backward, T={T} d={d} E={E} k={k} F={F} bf16, "
+                        "fp32 weight gradients",
+            "value": round(T * steps / elapsed, 1), "unit": "tokens/s",
+            "ms_per_step": round(elapsed / steps * 1e3, 4), "steps": steps, "stages": stages}
+
+
+def ep_bench(torch, moe, wl, dev, steps, warmup):
+    import moe_synth
+    idx, w = moe_synth.zipf_routing(wl, device=dev)
+    x = moe_synth.layer_inputs(wl, device=dev, with_experts=False)["x"]
+    lay = moe.Layout(wl.n_src, wl.n_dst, wl.cap_rows_per_dst)
+    plan = moe.moe_dispatch(x, idx, wl.E, layout=lay)
+    y = torch.empty_like(x)
+
+    def step(ev):
+        ev[0].record()
+        moe.moe_dispatch(x, idx, wl.E, layout=lay, out=plan)
+        ev[1].record()
+        moe.moe_combine(plan["x_disp"], plan["pair_slot"], w, y=y)   # identity experts
+        ev[2].record()
+
+    elapsed, events = timed(torch, step, 2, steps, warmup)
+    b, P = 2, wl.T * wl.k
+    work = {"dispatch": dict(bytes=wl.T * wl.d * b + P * wl.d * b, flops=0, unit="hbm"),
+            "combine": dict(bytes=P * wl.d * b + wl.T * wl.d * b + P * 8, flops=0, unit="hbm")}
+    stages = summarize(["dispatch", "combine"], events, steps, work)
+    live = plan["chunk_off"][:, -1]
+    out = {"workload": f"{wl.name}: rank-major dispatch + combine, {wl.n_src} sources x "
+                       f"{wl.tokens_per_src} tokens, d={wl.d} E={wl.E} k={wl.k}, Zipf({wl.zipf_s}), "
+                       f"{wl.cap_rows_per_dst} rows per destination",
+           "max_rows_per_dst": int(live.max()), "stages": stages}
+    del plan, x
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(wl, inp, target_s):
@@ -90,6 +269,16 @@ def cpu_baseline(wl, inp, target_s):
                       f"({total:.1f} s; float64 numpy FFN, float32 C router)"}
 
 
+def copy_probe(torch, mib):
+    n = mib * 1024 * 1024 // 2
+    src = torch.empty(n, dtype=torch.bfloat16, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_each_way": n * 2, "launches": 3}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -98,65 +287,26 @@ def main():
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
     import torch
+    if args.copy_probe_mib:
+        copy_probe(torch, args.copy_probe_mib)
+        return
     import moe_synth
     import token_routing_expert_router_amd as moe
 
     moe.load()
-    wl = moe_synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    inp = moe_synth.layer_inputs(wl, device=dev)
-    x, wr, w13, w2 = inp["x"], inp["w_router"], inp["w13"], inp["w2"]
+    if args.only_train:
+        ts = train_bench(torch, moe, moe_synth.WORKLOADS["mid_bf16_train"], dev, args.steps,
+                         args.warmup)
+        print(json.dumps({"train_step": ts}), flush=True)
+        return
+    wl = moe_synth.WORKLOADS[args.workload]
+    inp, elapsed, stages = forward_bench(torch, moe, wl, dev, args.steps, args.warmup)
     T, k, E, F, d = wl.T, wl.k, wl.E, wl.F, wl.d
-    dt = x.dtype
-
-    # every output allocated once; the timed loop allocates nothing
-    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
-    gates = torch.empty((T, k), dtype=torch.float32, device=dev)
-    plan = moe.moe_dispatch(x, moe.moe_route(x, wr, k)[0], E)
-    act = torch.empty((T * k, F), dtype=dt, device=dev)
-    y_disp = torch.empty((T * k, d), dtype=dt, device=dev)
-    y = torch.empty((T, d), dtype=dt, device=dev)
-    names = ["route", "dispatch", "gate_up", "down", "combine"]
-
-    def step(ev):
-        ev[0].record()
-        moe.moe_route(x, wr, k, topk_idx=idx, topk_w=gates)
-        ev[1].record()
-        moe.moe_dispatch(x, idx, E, out=plan)
-        ev[2].record()
-        moe.moe_expert_ffn_gate_up(plan["x_disp"], plan["expert_off"], w13, act=act)
-        ev[3].record()
-        moe.moe_expert_ffn_down(act, plan["expert_off"], w2, y_disp=y_disp)
-        ev[4].record()
-        moe.moe_combine(y_disp, plan["pair_slot"], gates, y=y)
-        ev[5].record()
-
-    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-    for _ in range(args.warmup):
-        step(mk())
-    events = [mk() for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    if moe.moe_dispatch_status(plan["ws"]) != 0:
-        raise RuntimeError("dispatch raised its device flag")
 
     work = stage_work(wl)
-    stages = {}
-    for s, name in enumerate(names):
-        ms = sum(ev[s].elapsed_time(ev[s + 1]) for ev in events) / args.steps
-        w = work[name]
-        bound, t_lb = bound_of(w)
-        st = {"us": round(ms * 1e3, 2), "GB_s": round(w["bytes"] / (ms * 1e-3) / 1e9, 1),
-              "bound": bound, "roofline_frac": round(t_lb / (ms * 1e-3), 3)}
-        if w["flops"]:
-            st["TFLOP_s"] = round(w["flops"] / (ms * 1e-3) / 1e12, 1)
-        stages[name] = st
-    dom = max(names, key=lambda n: stages[n]["us"])
+    dom = max(stages, key=lambda n: stages[n]["us"])
     w = work[dom]
     bound = stages[dom]["bound"]
     t = stages[dom]["us"] * 1e-6
@@ -169,7 +319,6 @@ def main():
                 "frac": round(achieved / peak, 4), "traffic": None, "kernel": dom,
                 "per_launch": per}
 
-    ms_step = elapsed / args.steps * 1e3
     line = {
         "metric": METRIC,
         "value": round(T * args.steps / elapsed, 1),
@@ -177,7 +326,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -191,6 +340,23 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+    del inp
+    torch.cuda.empty_cache()
+    if not args.no_extras and wl.dtype == "bf16":
+        line["train_step"] = train_bench(torch, moe, moe_synth.WORKLOADS["mid_bf16_train"], dev,
+                                         max(5, args.steps // 2), max(2, args.warmup // 2))
+        torch.cuda.empty_cache()
+        line["ep_dispatch_combine"] = ep_bench(torch, moe, moe_synth.WORKLOADS["ep32_zipf"], dev,
+                                               max(5, args.steps // 2), max(2, args.warmup // 2))
+        if not args.no_large:
+            lwl = moe_synth.WORKLOADS["large_bf16"]
+            linp, lel, lst = forward_bench(torch, moe, lwl, dev, 5, 2)
+            del linp
+            torch.cuda.empty_cache()
+            line["large"] = {"workload": f"{lwl.name}: MoE layer forward T={lwl.T} d={lwl.d} "
+                                         f"E={lwl.E} k={lwl.k} F={lwl.F} bf16, 34 GB weights",
+                             "value": round(lwl.T * 5 / lel, 1), "unit": "tokens/s",
+                             "ms_per_step": round(lel / 5 * 1e3, 4), "steps": 5, "stages": lst}
     print(json.dumps(line), flush=True)
 
 

@@ -27,43 +27,55 @@ namespace {
 
 enum { EPI_SWIGLU = 0, EPI_PLAIN = 1 };
 
-// Per-item state of the bf16 grouped GEMM: uniform bases, per-lane byte offsets of
-// the lane's 16-byte chunk in each of its wave's 8 A groups and 8 B groups.
+// Eight wavefronts, two per SIMD: wave w takes weight group w & 3 (64 weight rows)
+// and token group w >> 2 (128 token rows), so each SIMD holds one wave of each token
+// group and the MFMA work per SIMD is the same for any count of live token rows.
+constexpr int kFwdThreads = 512;
+constexpr int kLdsFwd = kLdsGemm;
+
+// silu(h) = h * sigmoid(h) with the hardware exp and reciprocal (the result is rounded
+// to bf16, far coarser than their error)
+__device__ __forceinline__ float silu_fast(float h) {
+    return h * __builtin_amdgcn_rcpf(1.0f + __expf(-h));
+}
+
+// Per-item state of the bf16 grouped GEMM: buffer resources of the token tile and
+// of the expert's weight panel, and per-lane byte offsets of the lane's 16-byte chunk
+// in each of its wave's 4 A groups and 4 B groups.
 struct GemmItem {
-    const char *Ab;          // first token row of the tile
-    const char *Wb;          // expert's weight panel
-    uint32_t a_off[8], b_off[8];
-    int a_groups;            // A groups (of 8 rows) holding live rows
-    int64_t m0, m_end;       // token rows [m0, m_end) are live in this tile
-    int n0;                  // first output column
+    __amdgpu_buffer_rsrc_t ra;   // token rows from the tile's first row on
+    __amdgpu_buffer_rsrc_t rw;   // the expert's weight panel
+    uint32_t a_off[4], b_off[4];
+    int a_groups;                // of this wave's 4 A groups, those holding live rows
+    int64_t m0, m_end;           // token rows [m0, m_end) are live in this tile
+    int n0;                      // first output column
 };
 
-// Direct global->LDS loads of one stage: wave w moves A groups w*8..w*8+7 and B
-// groups w*8..w*8+7, each one 1 KiB wavefront instruction.
+// Direct global->LDS loads of one stage: wave w moves A groups 4w..4w+3 and B groups
+// 4w..4w+3 (a group is 8 rows x 128 bytes, one 1 KiB wavefront instruction). Buffer
+// loads rather than global ones: the compiler then keeps its LDS waits exact.
 __device__ __forceinline__ void issue_stage(unsigned char *lds, int stage, int k0,
                                             const GemmItem &it, int wave) {
     unsigned char *As = lds + stage * (kLdsA + kLdsB);
     unsigned char *Bs = As + kLdsA;
-    const char *Ak = it.Ab + size_t(k0) * 2;
-    const char *Wk = it.Wb + size_t(k0) * 2;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 4; ++j) {
         if (j < it.a_groups)
-            __builtin_amdgcn_global_load_lds(
-                Ak + it.a_off[j], (__attribute__((address_space(3))) void *)(As + (wave * 8 + j) * 1024),
-                16, 0, 0);
-        __builtin_amdgcn_global_load_lds(
-            Wk + it.b_off[j], (__attribute__((address_space(3))) void *)(Bs + (wave * 8 + j) * 1024),
-            16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                it.ra, (__attribute__((address_space(3))) void *)(As + (wave * 4 + j) * 1024), 16,
+                it.a_off[j], k0 * 2, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            it.rw, (__attribute__((address_space(3))) void *)(Bs + (wave * 4 + j) * 1024), 16,
+            it.b_off[j], k0 * 2, 0, 0);
     }
 }
 
-// LDS reads of one k16 step: the wave's two weight fragments and NS token fragments
-// (16 bytes per lane each; rows are 128 B with chunk c stored at c ^ swz(row)).
-template <int NS>
+// LDS reads of one k16 step: the wave's two weight fragments and its NW token
+// fragments (16 bytes per lane each; rows are 128 B with chunk c stored at c ^ swz(row)).
+template <int NW>
 __device__ __forceinline__ void read_frags(const unsigned char *As, const unsigned char *Bs,
-                                           int lane, int ks, const int (&brow)[2],
-                                           bf16x8 (&wf)[2], bf16x8 (&tf)[NS]) {
+                                           int lane, int ks, const int (&brow)[2], int trow,
+                                           bf16x8 (&wf)[2], bf16x8 (&tf)[4]) {
     const int kc = ks * 2 + (lane >> 5);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -71,21 +83,24 @@ __device__ __forceinline__ void read_frags(const unsigned char *As, const unsign
         wf[s] = *reinterpret_cast<const bf16x8 *>(Bs + r * 128 + ((kc ^ swz(r)) << 4));
     }
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
-        const int r = i * 32 + (lane & 31);
+    for (int i = 0; i < NW; ++i) {
+        const int r = trow + i * 32 + (lane & 31);
         tf[i] = *reinterpret_cast<const bf16x8 *>(As + r * 128 + ((kc ^ swz(r)) << 4));
     }
 }
 
-// One work item with NS live 32-row token sub-tiles: the whole K loop and the
-// epilogue, branch-free in the inner loop.
-template <int EPI, int NS>
-__device__ __forceinline__ void run_item(unsigned char *lds, const GemmItem &it, int wave,
+// One work item, seen by one wave with NW (0..4) live 32-row token sub-tiles: the
+// whole K loop and the epilogue, branch-free in the inner loop. A wave with no live
+// rows still moves its share of every stage and joins every barrier.
+template <int EPI, int NW>
+__device__ __forceinline__ void run_item(unsigned char *lds, const GemmItem &it,
+                                         const GemmItem &next, bool has_next, int wave,
                                          int lane, int K, int N, uint16_t *__restrict__ out,
                                          uint16_t *__restrict__ hu_save) {
-    f32x16 acc[NS][2];
+    const int wn = wave & 3, wm = wave >> 2;
+    f32x16 acc[4][2];
 #pragma unroll
-    for (int i = 0; i < NS; ++i)
+    for (int i = 0; i < NW; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -95,56 +110,65 @@ __device__ __forceinline__ void run_item(unsigned char *lds, const GemmItem &it,
     int brow[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
-        brow[s] = (EPI == EPI_SWIGLU) ? s * 128 + wave * 32 : wave * 64 + s * 32;
+        brow[s] = (EPI == EPI_SWIGLU) ? s * 128 + wn * 32 : wn * 64 + s * 32;
+    const int trow = wm * 128;
 
     const int KT = K / BK;
-    __syncthreads();                 // the previous item's readers are done with LDS
-    issue_stage(lds, 0, 0, it, wave);
+    // stage 0 was issued before the previous item's epilogue (or before the first item)
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int kt = 0; kt < KT; ++kt) {
         const int cur = kt & 1;
         if (kt + 1 < KT) issue_stage(lds, cur ^ 1, (kt + 1) * BK, it, wave);
-        const unsigned char *As = lds + cur * (kLdsA + kLdsB);
-        const unsigned char *Bs = As + kLdsA;
-        // fragments double-buffered across the four k16 steps: the LDS reads of step
-        // ks+1 are issued before the MFMAs of step ks (sched_barrier keeps that order)
-        bf16x8 wf[2][2], tf[2][NS];
+        if (NW > 0) {
+            const unsigned char *As = lds + cur * (kLdsA + kLdsB);
+            const unsigned char *Bs = As + kLdsA;
+            // fragments double-buffered across the four k16 steps: the LDS reads of step
+            // ks+1 are issued before the MFMAs of step ks (sched_barrier keeps that order)
+            bf16x8 wf[2][2], tf[2][4];
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            if (ks == 0) {
-                read_frags<NS>(As, Bs, lane, 0, brow, wf[0], tf[0]);
+            for (int ks = 0; ks < BK / 16; ++ks) {
+                if (ks == 0) {
+                    read_frags<NW>(As, Bs, lane, 0, brow, trow, wf[0], tf[0]);
+                    __builtin_amdgcn_sched_barrier(0);   // step 0's reads issue first
+                }
+                if (ks + 1 < BK / 16)
+                    read_frags<NW>(As, Bs, lane, ks + 1, brow, trow, wf[(ks + 1) & 1], tf[(ks + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < NW; ++i)
+#pragma unroll
+                    for (int s = 0; s < 2; ++s)
+                        acc[i][s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks & 1][s], tf[ks & 1][i],
+                                                                            acc[i][s], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            if (ks + 1 < BK / 16) read_frags<NS>(As, Bs, lane, ks + 1, brow, wf[(ks + 1) & 1], tf[(ks + 1) & 1]);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int i = 0; i < NS; ++i)
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    acc[i][s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks & 1][s], tf[ks & 1][i], acc[i][s], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the next stage landed
         __syncthreads();                 // everyone's loads landed, and cur is free
     }
 
+    // every wave is past its last LDS read: the next item's first stage flies during
+    // this item's epilogue
+    if (has_next) issue_stage(lds, 0, 0, next, wave);
+
     // epilogue: D = W_tile * X_tile^T, so lane l holds token column m = l & 31 and, for
     // v = 4g + q, weight row n = 8g + 4*(l >> 5) + q: four consecutive outputs of one
     // token row, stored as one 8-byte write per (sub-tile, g)
-    const int64_t mrow0 = it.m0 + (lane & 31);
+    const int64_t mrow0 = it.m0 + trow + (lane & 31);
     const int nl = 4 * (lane >> 5);
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
+    for (int i = 0; i < NW; ++i) {
         const int64_t m = mrow0 + i * 32;
         if (m >= it.m_end) continue;
         if (EPI == EPI_SWIGLU) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int n = it.n0 + wave * 32 + 8 * g + nl;
+                const int n = it.n0 + wn * 32 + 8 * g + nl;
                 if (n >= N) continue;
                 float a4[4];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) a4[q] = silu_f(acc[i][0][4 * g + q]) * acc[i][1][4 * g + q];
+                for (int q = 0; q < 4; ++q) a4[q] = silu_fast(acc[i][0][4 * g + q]) * acc[i][1][4 * g + q];
                 uint2 pa;
                 pa.x = pack_bf16x2(a4[0], a4[1]);
                 pa.y = pack_bf16x2(a4[2], a4[3]);
@@ -164,7 +188,7 @@ __device__ __forceinline__ void run_item(unsigned char *lds, const GemmItem &it,
             for (int s = 0; s < 2; ++s)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const int n = it.n0 + wave * 64 + s * 32 + 8 * g + nl;
+                    const int n = it.n0 + wn * 64 + s * 32 + 8 * g + nl;
                     if (n >= N) continue;
                     uint2 p;
                     p.x = pack_bf16x2(acc[i][s][4 * g], acc[i][s][4 * g + 1]);
@@ -175,8 +199,59 @@ __device__ __forceinline__ void run_item(unsigned char *lds, const GemmItem &it,
     }
 }
 
+// Work item -> per-wave load state. An expert's rows are split into equal m-tiles, so
+// the tiles that share one weight panel run at one speed and meet in L2; rows past the
+// allocation are never touched, whatever expert_off holds.
 template <int EPI>
-__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_bf16(
+__device__ __forceinline__ GemmItem make_item(int item, const int *tile_off,
+                                              const int *__restrict__ expert_off, int E,
+                                              int n_tiles, const uint16_t *__restrict__ A,
+                                              const uint16_t *__restrict__ W, int K, int N,
+                                              int64_t rows_alloc, int wave, int lane) {
+    const int Nw = (EPI == EPI_SWIGLU) ? 2 * N : N;              // weight rows per expert
+    // a direct load puts lane l's 16 bytes at row l/8, physical chunk l%8 of its
+    // 8-row group, so the XOR swizzle is applied on the global side
+    const int lrow = lane >> 3;
+    const int pchunk = lane & 7;
+    const ItemCoord ic = decode_item(item, tile_off, E, n_tiles);
+    const int e = ic.e;
+    GemmItem it;
+    const int64_t e_lo = min<int64_t>(expert_off[e], rows_alloc);
+    const int64_t e_hi = min<int64_t>(expert_off[e + 1], rows_alloc);
+    const int mc = tile_off[e + 1] - tile_off[e];
+    const int64_t rp = (e_hi - e_lo + mc - 1) / mc;     // <= BM
+    it.m0 = e_lo + int64_t(ic.mt) * rp;
+    it.m_end = min<int64_t>(e_hi, it.m0 + rp);
+    it.n0 = ic.nt * (EPI == EPI_SWIGLU ? BNW / 2 : BNW);
+    // byte ranges of the two resources (loads past them would read zeros); the host
+    // bounds the weight panel below 2^31 bytes
+    it.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(A + it.m0 * K), 0,
+                                             int((rows_alloc - it.m0 < BM ? rows_alloc - it.m0 : BM) * K * 2),
+                                             0x00020000);
+    it.rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(W + size_t(e) * Nw * K), 0,
+                                             int(size_t(Nw) * K * 2), 0x00020000);
+    it.a_groups = int(min<int64_t>(4, max<int64_t>(0, (it.m_end - it.m0 - wave * 32 + 7) / 8)));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int g = wave * 4 + j;
+        const int r = g * 8 + lrow;              // tile row 0..255
+        const int c = pchunk ^ swz(r);
+        const int64_t tr = min<int64_t>(it.m0 + r, rows_alloc - 1);
+        it.a_off[j] = uint32_t(((tr - it.m0) * K + c * 8) * 2);
+        int wr;
+        if (EPI == EPI_SWIGLU) {
+            const int n = min(it.n0 + (r & 127), N - 1);
+            wr = (r < 128) ? n : N + n;
+        } else {
+            wr = min(it.n0 + r, N - 1);
+        }
+        it.b_off[j] = uint32_t((size_t(wr) * K + c * 8) * 2);
+    }
+    return it;
+}
+
+template <int EPI>
+__global__ __launch_bounds__(kFwdThreads) void k_gemm_bf16(
     const uint16_t *__restrict__ A,        // token rows [rows, K]
     const int *__restrict__ expert_off,    // [E+1]
     int E, const uint16_t *__restrict__ W, // [E, Nw, K]
@@ -190,64 +265,38 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_bf16(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wavefront
-    const int Nw = (EPI == EPI_SWIGLU) ? 2 * N : N;              // weight rows per expert
     build_tile_map(expert_off, E, BM, rows_alloc, tile_off, map_scratch);
     const int total = tile_off[E] * n_tiles;
     const int G = gridDim.x;
-    // this workgroup's place in a round: XCD (blockIdx % 8) gets a contiguous run
+    // this workgroup's place in a round: XCD (blockIdx % 8) gets a contiguous run;
+    // rotating the place each round spreads large and small items evenly
     const int per = G / 8;
     const int slot = (G % 8 == 0) ? (blockIdx.x % 8) * per + blockIdx.x / 8 : blockIdx.x;
-    // A direct load puts lane l's 16 bytes at row l/8, physical chunk l%8 of its
-    // 8-row group, so the XOR swizzle is applied on the global side
-    const int lrow = lane >> 3;
-    const int pchunk = lane & 7;
+    if (slot >= total) return;
 
+    GemmItem it = make_item<EPI>(slot, tile_off, expert_off, E, n_tiles, A, W, K, N, rows_alloc,
+                                 wave, lane);
+    issue_stage(lds, 0, 0, it, wave);
     for (int base = 0; base < total; base += G) {
-        const int item = base + slot;
-        if (item >= total) break;
-        const int mt = item / n_tiles, nt = item % n_tiles;
-        int lo = 0, hi = E;                          // expert owning m-tile mt
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (tile_off[mid] <= mt) lo = mid; else hi = mid;
-        }
-        const int e = lo;
-        GemmItem it;
-        it.m0 = int64_t(expert_off[e]) + int64_t(mt - tile_off[e]) * BM;
-        // rows past the allocation are never written, whatever expert_off holds
-        it.m_end = min<int64_t>(expert_off[e + 1], rows_alloc);
-        it.n0 = nt * (EPI == EPI_SWIGLU ? BNW / 2 : BNW);
-        it.Ab = reinterpret_cast<const char *>(A + it.m0 * K);
-        it.Wb = reinterpret_cast<const char *>(W + size_t(e) * Nw * K);
-        it.a_groups = 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int g = wave * 8 + j;
-            const int r = g * 8 + lrow;              // tile row 0..255
-            const int c = pchunk ^ swz(r);
-            const int64_t tr = min<int64_t>(it.m0 + r, rows_alloc - 1);
-            it.a_off[j] = uint32_t(((tr - it.m0) * K + c * 8) * 2);
-            if (it.m0 + g * 8 < it.m_end) it.a_groups = j + 1;
-            int wr;
-            if (EPI == EPI_SWIGLU) {
-                const int n = min(it.n0 + (r & 127), N - 1);
-                wr = (r < 128) ? n : N + n;
-            } else {
-                wr = min(it.n0 + r, N - 1);
-            }
-            it.b_off[j] = uint32_t((size_t(wr) * K + c * 8) * 2);
-        }
+        const int nbase = base + G;
+        const int nitem = nbase + (slot + nbase / G) % G;
+        const bool has_next = nitem < total;
+        GemmItem next = it;
+        if (has_next)
+            next = make_item<EPI>(nitem, tile_off, expert_off, E, n_tiles, A, W, K, N, rows_alloc,
+                                  wave, lane);
+        // live 32-row token sub-tiles of this wave's token group
         const int nsub = int(min<int64_t>(8, (it.m_end - it.m0 + 31) / 32));
-        switch (nsub) {
-        case 8: run_item<EPI, 8>(lds, it, wave, lane, K, N, out, hu_save); break;
-        case 7: run_item<EPI, 7>(lds, it, wave, lane, K, N, out, hu_save); break;
-        case 6: run_item<EPI, 6>(lds, it, wave, lane, K, N, out, hu_save); break;
-        case 5: run_item<EPI, 5>(lds, it, wave, lane, K, N, out, hu_save); break;
-        case 4: run_item<EPI, 4>(lds, it, wave, lane, K, N, out, hu_save); break;
-        case 3: run_item<EPI, 3>(lds, it, wave, lane, K, N, out, hu_save); break;
-        case 2: run_item<EPI, 2>(lds, it, wave, lane, K, N, out, hu_save); break;
-        default: run_item<EPI, 1>(lds, it, wave, lane, K, N, out, hu_save); break;
+        const int nw = min(4, max(0, nsub - (wave >> 2) * 4));
+        switch (nw) {
+        case 4: run_item<EPI, 4>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
+        case 3: run_item<EPI, 3>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
+        case 2: run_item<EPI, 2>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
+        case 1: run_item<EPI, 1>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
+        default: run_item<EPI, 0>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
         }
+        if (!has_next) break;
+        it = next;
     }
 }
 
@@ -273,14 +322,9 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float *__restrict__ A,
     build_tile_map(expert_off, E, FT, rows_alloc, tile_off, map_scratch);
     const int total = tile_off[E] * n_tiles;
     for (int item = blockIdx.x; item < total; item += gridDim.x) {
-        const int mt = item / n_tiles, nt = item % n_tiles;
-        int lo = 0, hi = E;
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (tile_off[mid] <= mt) lo = mid; else hi = mid;
-        }
-        const int e = lo;
-        const int m0 = expert_off[e] + (mt - tile_off[e]) * FT;
+        const ItemCoord ic = decode_item(item, tile_off, E, n_tiles);
+        const int e = ic.e, nt = ic.nt;
+        const int m0 = expert_off[e] + ic.mt * FT;
         const int m_end = int(min<int64_t>(expert_off[e + 1], rows_alloc));
         const int n0 = nt * FT;
         const float *We = W + size_t(e) * Nw * K;
@@ -343,9 +387,9 @@ bool set_lds_limits() {
     static std::once_flag once;
     std::call_once(once, [] {
         ok = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_bf16<EPI_SWIGLU>),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, kLdsGemm) == hipSuccess &&
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, kLdsFwd) == hipSuccess &&
              hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_bf16<EPI_PLAIN>),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, kLdsGemm) == hipSuccess;
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, kLdsFwd) == hipSuccess;
     });
     return ok;
 }
@@ -360,6 +404,8 @@ moe_status_t check_common(int32_t E, int64_t rows, int64_t d, int64_t F, moe_dty
     if (E > kMaxE || rows >= (int64_t(1) << 31) || d > (1 << 20) || F > (1 << 20))
         return MOE_ERR_UNSUPPORTED;
     if (dtype == MOE_BF16 && (d % BK != 0 || F % BK != 0)) return MOE_ERR_UNSUPPORTED;
+    // one expert's weight panel (2F x d or d x F) is addressed with 32-bit byte offsets
+    if (2 * F * d * int64_t(elt_size(dtype)) >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
     if ((d * elt_size(dtype)) % 16 != 0 || (F * elt_size(dtype)) % 16 != 0) return MOE_ERR_ALIGN;
     return MOE_OK;
 }
@@ -371,7 +417,7 @@ moe_status_t launch_gate_up(const void *x_disp, const int32_t *expert_off, const
         if (!set_lds_limits()) return MOE_ERR_HIP;
         const int nt = int(cdiv(F, BNW / 2));
         const int g = int(std::min<int64_t>((cdiv(rows, BM) + E) * nt, num_cus()));
-        hipLaunchKernelGGL(k_gemm_bf16<EPI_SWIGLU>, dim3(g), dim3(kGemmThreads), kLdsGemm, st,
+        hipLaunchKernelGGL(k_gemm_bf16<EPI_SWIGLU>, dim3(g), dim3(kFwdThreads), kLdsFwd, st,
                            static_cast<const uint16_t *>(x_disp), expert_off, E,
                            static_cast<const uint16_t *>(w13), int(d), int(F), rows,
                            static_cast<uint16_t *>(act), static_cast<uint16_t *>(hu_save), nt);
@@ -393,7 +439,7 @@ moe_status_t launch_down(const void *act, const int32_t *expert_off, const void 
         if (!set_lds_limits()) return MOE_ERR_HIP;
         const int nt = int(cdiv(d, BNW));
         const int g = int(std::min<int64_t>((cdiv(rows, BM) + E) * nt, num_cus()));
-        hipLaunchKernelGGL(k_gemm_bf16<EPI_PLAIN>, dim3(g), dim3(kGemmThreads), kLdsGemm, st,
+        hipLaunchKernelGGL(k_gemm_bf16<EPI_PLAIN>, dim3(g), dim3(kFwdThreads), kLdsFwd, st,
                            static_cast<const uint16_t *>(act), expert_off, E,
                            static_cast<const uint16_t *>(w2), int(F), int(d), rows,
                            static_cast<uint16_t *>(y_disp), nullptr, nt);

@@ -310,22 +310,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_bwd(BwdArgs A, int t_t
     const int per = G / 8;
     const int slot = (G % 8 == 0) ? (blockIdx.x % 8) * per + blockIdx.x / 8 : blockIdx.x;
     for (int base = 0; base < total; base += G) {
-        const int item = base + slot;
+        // rotating the slot each round spreads large and small items evenly
+        const int item = base + (slot + base / G) % G;
         if (item >= total) break;
         BwdItem it;
         int nsub;
         if (DGRAD) {
-            const int mt = item / n_tiles, nt = item % n_tiles;
-            int lo = 0, hi = E;
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (tile_off[mid] <= mt) lo = mid; else hi = mid;
-            }
-            it.e = lo;
-            it.m0 = int64_t(A.expert_off[lo]) + int64_t(mt - tile_off[lo]) * BM;
-            it.m_end = min<int64_t>(A.expert_off[lo + 1], A.rows_alloc);
+            const ItemCoord ic = decode_item(item, tile_off, E, n_tiles);
+            it.e = ic.e;
+            it.m0 = int64_t(A.expert_off[ic.e]) + int64_t(ic.mt) * BM;
+            it.m_end = min<int64_t>(A.expert_off[ic.e + 1], A.rows_alloc);
             it.t0 = 0;
-            it.n0 = nt * BNW;
+            it.n0 = ic.nt * BNW;
             it.KT = Kd / BK;
             nsub = int(min<int64_t>(8, (it.m_end - it.m0 + 31) / 32));
         } else {
