@@ -256,7 +256,7 @@ def cpu_baseline(wl, inp, target_s):
     import oracle
     host = {n: t.cpu() for n, t in inp.items()}
     n, total = 0, 0.0
-    while n < 3 and (total < target_s or n == 0):
+    while n < 10 and (total < target_s or n == 0):
         t0 = time.perf_counter()
         oracle.forward(host["x"], host["w_router"], host["w13"], host["w2"], wl.k)
         total += time.perf_counter() - t0
@@ -267,6 +267,36 @@ def cpu_baseline(wl, inp, target_s):
             "kind": "oracle",
             "sample": f"{n} full forward pass(es) of the {wl.T}-token workload "
                       f"({total:.1f} s; float64 numpy FFN, float32 C router)"}
+
+
+# Sources that define the grouped-GEMM kernels; a traffic record taken with other
+# sources no longer describes the kernel and is not reported.
+KERNEL_SOURCES = ("token_routing_expert_router_amd/csrc/ffn.hip",
+                  "token_routing_expert_router_amd/csrc/gemm_common.h",
+                  "token_routing_expert_router_amd/csrc/common.h")
+TRAFFIC_RECORD = "profiles/gate_up_T4096_d2048_E64_k6_F1408_hbm_traffic.json"
+
+
+def kernel_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE record,
+    or None if there is none for it or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, TRAFFIC_RECORD)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("stage") != kernel or rec.get("source_sha256") != kernel_source_digest():
+        return None
+    return int(rec["traffic_bytes_per_launch"])
 
 
 def copy_probe(torch, mib):
@@ -316,7 +346,7 @@ def main():
         peak = PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_FP32_VALU_TFLOPS
         achieved, unit, per = w["flops"] / t / 1e12, "TFLOP/s", w["flops"]
     roofline = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": None, "kernel": dom,
+                "frac": round(achieved / peak, 4), "traffic": measured_traffic(dom), "kernel": dom,
                 "per_launch": per}
 
     line = {
