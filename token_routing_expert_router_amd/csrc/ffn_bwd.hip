@@ -1,18 +1,20 @@
-// Backward of the expert FFN: four grouped GEMMs per expert, on the same 256 x 256 x 64
-// MFMA tile as the forward. With X, dO = dy_disp rows of expert e, h, u from the
-// forward (hu_save), a = silu(h) * u:
+// Backward of the expert FFN: four grouped GEMMs per expert on a 256 x 256 x 64 MFMA
+// tile, eight wavefronts per workgroup as in the forward. With X, dO = dy_disp rows of
+// expert e, h, u from the forward (hu_save), a = silu(h) * u:
 //   G1  dA = dO W2            epilogue: dh = dA u s (1 + h (1 - s)), du = dA silu(h)
-//                             (s = sigmoid(h)), stored as dHU = [dh du] in bf16
+//                             (s = sigmoid(h)), stored as dHU = [dh du] in bf16, and a
+//                             recomputed from h, u for G3
 //   G2  dX = dHU W13          -> dx_disp (bf16)
 //   G3  dW2 = dO^T a          -> dw2  (fp32), contraction over the expert's rows
 //   G4  dW13 = dHU^T X        -> dw13 (fp32), contraction over the expert's rows
-// Every one of them contracts over a dimension that is strided in at least one
-// operand, so next to the direct global->LDS loads of the forward there is a
-// transposing loader: a thread fetches an 8 (k) x 8 (n) block of bf16 with eight
-// 16-byte loads, transposes it in registers with v_perm_b32 and writes eight
-// K-contiguous 16-byte rows into the same swizzled LDS layout, so the MFMA fragment
-// reads are unchanged. Reductions over rows run in one fixed order per output
-// (stages in row order, MFMA k order inside), so results are bitwise reproducible.
+// The MFMA's A operand indexes the output's contiguous dimension and its B operand the
+// output rows. Every A operand, and the B operand of G3/G4, is stored with the
+// contraction dimension strided: such a tile is copied to LDS as it lies in memory (k
+// rows of 256 contiguous elements, direct loads) and transposed on the way out by
+// ds_read_b64_tr_b16, whose 16-lane groups hand lane 4a+b element b of the 8-byte
+// pieces read by lanes a, a+4, a+8, a+12. Reductions over rows run in one fixed order
+// per output (stages in row order, MFMA k order inside), so results are bitwise
+// reproducible.
 #include "gemm_common.h"
 
 namespace moe {
@@ -20,250 +22,307 @@ namespace {
 
 enum { G1_DA = 0, G2_DX = 1, G3_DW2 = 2, G4_DW13 = 3 };
 
+constexpr int kBwdThreads = 512;     // 8 waves: 4 A groups (64 rows) x 2 B groups (128 rows)
+
 struct BwdArgs {
     const uint16_t *x_disp, *dy_disp, *hu, *w13, *w2;
     const int *expert_off;
-    uint16_t *dhu, *dx_disp;
+    uint16_t *dhu, *act, *dx_disp;
     float *dw13, *dw2;
     int E, d, F;
     int64_t rows_alloc;
 };
 
-// 8 x 8 block of bf16: reg[r] holds row krow0 + r (8 elements along n) of the stage
-// that starts at the uniform byte pointer `base` (rows ldb bytes apart). Rows at or
-// past kvalid, or a block with nok false, read as zero; their loads go to row 0 of
-// the stage (always inside the matrix) so the code stays branch-free.
-__device__ __forceinline__ void tload(u32x4 (&reg)[8], const char *base, uint32_t ldb, int krow0,
-                                      int kvalid, uint32_t noff, bool nok) {
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Transposed tiles: 64 k rows of 512 B (256 elements); 16-byte chunk c of k row r lives
+// at chunk c ^ swzT(r), so the four k rows one transposing read touches fall on
+// distinct bank groups.
+__device__ __forceinline__ int swzT(int r) { return (r & 3) << 2; }
+
+// One operand's load state for the current item: where its tile data starts, how many
+// bytes from there belong to it (loads past them read zeros), and the lane's byte offset
+// for the even and the odd ones of the wave's four 1 KiB direct-load instructions of a
+// stage (instruction j + 2 reads jstep bytes further on than instruction j).
+struct Opnd {
+    const char *base;
+    int64_t nbytes;
+    uint32_t off[2];
+    uint32_t jstep;
+    uint32_t kstep;          // bytes between consecutive stages
+};
+
+// Normal operand (rows K-contiguous, `ld` elements apart; at most 256 rows, so the
+// byte count fits a buffer resource): instruction j of wave w moves tile rows
+// 8(4w+j) .. +7 (128 B each); stages advance along the rows.
+__device__ __forceinline__ void opnd_normal(Opnd &o, const uint16_t *base, int64_t nbytes, int ld,
+                                            int wave, int lane) {
+    o.base = reinterpret_cast<const char *>(base);
+    o.nbytes = nbytes;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        const int kr = krow0 + r;
-        const bool ok = nok && kr < kvalid;
-        const uint32_t off = uint32_t(ok ? kr : 0) * ldb + (nok ? noff : 0u);
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(base + off);
-        reg[r] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+    for (int j = 0; j < 2; ++j) {
+        const int r = (wave * 4 + j) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz(r);      // swz(r + 16) == swz(r)
+        o.off[j] = uint32_t((r * ld + c * 8) * 2);
     }
+    o.jstep = uint32_t(16 * ld * 2);
+    o.kstep = BK * 2;
 }
 
-// reg[r] <- bf16(silu(h) * u) with h = reg[r], u = ureg[r] (8 values each)
-__device__ __forceinline__ void swiglu_rows(u32x4 (&reg)[8], const u32x4 (&ureg)[8]) {
+// Transposed operand (k rows `ld` elements apart, the tile's 256 columns from col0):
+// instruction j of wave w moves k rows 2(4w+j), 2(4w+j)+1 of the stage; stages advance
+// by 64 k rows, and each stage gets its own resource, so the byte count may exceed
+// what one resource can describe.
+__device__ __forceinline__ void opnd_trans(Opnd &o, const uint16_t *base, int64_t nbytes, int ld,
+                                           int col0, int wave, int lane) {
+    o.base = reinterpret_cast<const char *>(base);
+    o.nbytes = nbytes;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        uint32_t o[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t hv = reg[r][j], uv = ureg[r][j];
-            o[j] = pack_bf16x2(silu_f(bf16_lo(hv)) * bf16_lo(uv), silu_f(bf16_hi(hv)) * bf16_hi(uv));
-        }
-        reg[r] = u32x4{o[0], o[1], o[2], o[3]};
+    for (int j = 0; j < 2; ++j) {
+        const int kr = (wave * 4 + j) * 2 + (lane >> 5);
+        const int c = (lane & 31) ^ swzT(kr);   // swzT(kr + 4) == swzT(kr)
+        o.off[j] = uint32_t((kr * ld + col0 + c * 8) * 2);
     }
+    o.jstep = uint32_t(4 * ld * 2);
+    o.kstep = uint32_t(BK * ld * 2);
 }
 
-// Transpose the 8 x 8 block and store its 8 columns as K-contiguous 16-byte chunks:
-// LDS row nb*8 + c (the n index), logical chunk kb (the k block), swizzled.
-__device__ __forceinline__ void tstore(const u32x4 (&reg)[8], unsigned char *tile, int nb, int kb) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        const int j = c >> 1;
-        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
-        u32x4 o;
-        o.x = __builtin_amdgcn_perm(reg[1][j], reg[0][j], sel);
-        o.y = __builtin_amdgcn_perm(reg[3][j], reg[2][j], sel);
-        o.z = __builtin_amdgcn_perm(reg[5][j], reg[4][j], sel);
-        o.w = __builtin_amdgcn_perm(reg[7][j], reg[6][j], sel);
-        const int row = nb * 8 + c;
-        *reinterpret_cast<u32x4 *>(tile + row * 128 + ((kb ^ swz(row)) << 4)) = o;
-    }
+// The four direct loads are written as assembly: the compiler then has no LDS write of
+// its own to order the transposing reads against (it would wait for every load in
+// flight, the next stage's included, before each of them). The kernel orders them
+// itself: each stage ends with s_waitcnt vmcnt(0) and a barrier before anyone reads it.
+__device__ __forceinline__ void dma16(unsigned char *dst, __amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                      uint32_t soff) {
+    // m0 and soffset are wave-uniform; readfirstlane keeps them in scalar registers
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) unsigned char *)dst)));
+    const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(m0), "v"(voff), "s"(rs), "s"(so) : "memory", "m0");
 }
 
-template <int NS>
-__device__ __forceinline__ void mma_stage(const unsigned char *Ts, const unsigned char *Ws, int lane,
-                                          const int (&brow)[2], f32x16 (&acc)[NS][2]) {
-    bf16x8 wf[2][2], tf[2][NS];
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-        auto rd = [&](int kss, bf16x8 (&w)[2], bf16x8 (&t)[NS]) {
-            const int kc = kss * 2 + (lane >> 5);
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int r = brow[s] + (lane & 31);
-                w[s] = *reinterpret_cast<const bf16x8 *>(Ws + r * 128 + ((kc ^ swz(r)) << 4));
-            }
-#pragma unroll
-            for (int i = 0; i < NS; ++i) {
-                const int r = i * 32 + (lane & 31);
-                t[i] = *reinterpret_cast<const bf16x8 *>(Ts + r * 128 + ((kc ^ swz(r)) << 4));
-            }
-        };
-        if (ks == 0) rd(0, wf[0], tf[0]);
-        if (ks + 1 < BK / 16) rd(ks + 1, wf[(ks + 1) & 1], tf[(ks + 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < NS; ++i)
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-                acc[i][s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks & 1][s], tf[ks & 1][i], acc[i][s], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+template <bool TR>
+__device__ __forceinline__ void issue_opnd(unsigned char *tile, const Opnd &o, int kt, int wave) {
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t soff;
+    if (TR) {
+        const int64_t start = int64_t(kt) * o.kstep;
+        const int64_t rem = o.nbytes - start;        // > 0: stages start inside the data
+        rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(o.base + start), 0,
+                                               int(rem < 0x7fffffff ? rem : 0x7fffffff), 0x00020000);
+        soff = 0;
+    } else {
+        rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(o.base), 0, int(o.nbytes), 0x00020000);
+        soff = uint32_t(kt) * o.kstep;
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        dma16(tile + (wave * 4 + j) * 1024, rs, o.off[j & 1], soff + uint32_t(j >> 1) * o.jstep);
+}
+
+// MFMA fragment (32 rows from row0, k16 step ks) of a normal tile
+__device__ __forceinline__ bf16x8 frag_normal(const unsigned char *tile, int row0, int ks, int lane) {
+    const int r = row0 + (lane & 31);
+    const int kc = ks * 2 + (lane >> 5);
+    return *reinterpret_cast<const bf16x8 *>(tile + r * 128 + ((kc ^ swz(r)) << 4));
+}
+
+// The same fragment of a transposed tile: lane l needs rows row0 + (l & 31), k values
+// 16 ks + 8 (l >> 5) + 0..7; source lane s of its 16-lane group points at k row
+// (s >> 2) (+4 for the second read) and the four columns 4 (s & 3) .. +3 of its half.
+__device__ __forceinline__ bf16x8 frag_trans(const unsigned char *tile, int row0, int ks, int lane) {
+    const int s = lane & 15;
+    const int kr = ks * 16 + 8 * (lane >> 5) + (s >> 2);
+    const int m = row0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+    const int off = kr * 512 + (((m >> 3) ^ swzT(kr)) << 4) + (m & 7) * 2;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(tile + off));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(tile + off + 4 * 512));
+    const s16x4 v8[2] = {lo, hi};
+    return __builtin_bit_cast(bf16x8, v8);
+}
+
+template <bool TR>
+__device__ __forceinline__ bf16x8 frag(const unsigned char *tile, int row0, int ks, int lane) {
+    if (TR) return frag_trans(tile, row0, ks, lane);
+    return frag_normal(tile, row0, ks, lane);
 }
 
 struct BwdItem {
+    Opnd a, b;               // A: output columns, B: output rows
     int e;
-    int64_t m0, m_end;   // the expert's token rows used by this item
-    int t0;              // first T-side row (output row) of the tile
-    int n0;              // first W-side row (output column) of the tile
-    int KT;              // LDS stages
+    int64_t m0, m_end;       // the expert's token rows used by this item
+    int a0, b0;              // first output column / output row of the tile (matrix coords)
+    int KT;                  // LDS stages
 };
 
-template <int KIND, int NS>
-__device__ __forceinline__ void run_bwd_item(unsigned char *lds, const BwdArgs &A, const BwdItem &it,
-                                             int wave, int lane) {
+template <int KIND>
+__device__ __forceinline__ BwdItem make_bwd_item(const BwdArgs &A, int item, const int *tile_off,
+                                                 int t_tiles, int n_tiles, int wave, int lane) {
     constexpr bool DGRAD = (KIND == G1_DA || KIND == G2_DX);
-    const int tid = threadIdx.x;
-    const int d = A.d, F = A.F;
-    const int F2 = 2 * F;
-
-    // ---------------- operand geometry
-    // T side (MFMA B, 256 rows shared by all waves)
-    const uint16_t *Tsrc;        // DGRAD: token rows (direct); WGRAD: [K=rows][N] matrix
-    int64_t ldT;
-    int nT;                      // WGRAD: size of the T side
-    if (KIND == G1_DA) { Tsrc = A.dy_disp; ldT = d; nT = 0; }
-    else if (KIND == G2_DX) { Tsrc = A.dhu; ldT = F2; nT = 0; }
-    else if (KIND == G3_DW2) { Tsrc = A.dy_disp; ldT = d; nT = d; }
-    else { Tsrc = A.dhu; ldT = F2; nT = F2; }
-    // W side (MFMA A, 64 rows per wave), always loaded through the transposing path
-    const uint16_t *Wsrc;
-    int64_t ldW;
-    int nW;
-    int64_t k_endW;
-    if (KIND == G1_DA) { Wsrc = A.w2 + size_t(it.e) * d * F; ldW = F; nW = F; k_endW = d; }
-    else if (KIND == G2_DX) { Wsrc = A.w13 + size_t(it.e) * F2 * d; ldW = d; nW = d; k_endW = F2; }
-    else if (KIND == G3_DW2) { Wsrc = A.hu; ldW = F2; nW = F; k_endW = it.m_end; }
-    else { Wsrc = A.x_disp; ldW = d; nW = d; k_endW = it.m_end; }
-    const int64_t kW0 = DGRAD ? 0 : it.m0;     // first k row of the W side
-
-    const int nb = tid & 31, kb = tid >> 5;    // this thread's 8 x 8 block of a 256 x 64 tile
-
-    // direct-load offsets of the T side (DGRAD only), as in the forward
-    uint32_t a_off[8];
-    int a_groups = 0;
-    const char *Tb = nullptr;
+    const int d = A.d, F = A.F, F2 = 2 * F;
+    BwdItem it;
     if (DGRAD) {
-        const int lrow = lane >> 3, pchunk = lane & 7;
-        Tb = reinterpret_cast<const char *>(Tsrc + it.m0 * ldT);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int g = wave * 8 + j;
-            const int r = g * 8 + lrow;
-            const int c = pchunk ^ swz(r);
-            const int64_t tr = min<int64_t>(it.m0 + r, A.rows_alloc - 1);
-            a_off[j] = uint32_t(((tr - it.m0) * ldT + c * 8) * 2);
-            if (it.m0 + g * 8 < it.m_end) a_groups = j + 1;
+        const ItemCoord ic = decode_item(item, tile_off, A.E, n_tiles);
+        it.e = ic.e;
+        const int64_t e_lo = min<int64_t>(A.expert_off[ic.e], A.rows_alloc);
+        const int64_t e_hi = min<int64_t>(A.expert_off[ic.e + 1], A.rows_alloc);
+        const int mc = tile_off[ic.e + 1] - tile_off[ic.e];
+        const int64_t rp = (e_hi - e_lo + mc - 1) / mc;     // equal m-tiles, <= BM
+        it.m0 = e_lo + int64_t(ic.mt) * rp;
+        it.m_end = min<int64_t>(e_hi, it.m0 + rp);
+        it.a0 = ic.nt * BNW;
+        it.b0 = 0;
+        const int K = (KIND == G1_DA) ? d : F2;
+        it.KT = K / BK;
+        // B: the tile's token rows of dO (G1) or dHU (G2); rows past m_end read zeros
+        const uint16_t *tb = (KIND == G1_DA) ? A.dy_disp : A.dhu;
+        opnd_normal(it.b, tb + it.m0 * K, (it.m_end - it.m0) * K * 2, K, wave, lane);
+        // A: W2_e [d][F] (G1) or W13_e [2F][d] (G2), k rows along the contraction
+        if (KIND == G1_DA)
+            opnd_trans(it.a, A.w2 + size_t(it.e) * d * F, int64_t(d) * F * 2, F, it.a0, wave, lane);
+        else
+            opnd_trans(it.a, A.w13 + size_t(it.e) * F2 * d, int64_t(F2) * d * 2, d, it.a0, wave, lane);
+    } else {
+        it.e = item / (t_tiles * n_tiles);
+        const int rem = item % (t_tiles * n_tiles);
+        it.b0 = (rem / n_tiles) * BM;
+        it.a0 = (rem % n_tiles) * BNW;
+        it.m0 = min<int64_t>(A.expert_off[it.e], A.rows_alloc);
+        it.m_end = max(it.m0, min<int64_t>(A.expert_off[it.e + 1], A.rows_alloc));
+        it.KT = int((it.m_end - it.m0 + BK - 1) / BK);
+        const int64_t nr = it.m_end - it.m0;               // rows past these read zeros
+        if (KIND == G3_DW2) {        // dW2[i][f] = sum_r dO[r][i] a[r][f]
+            opnd_trans(it.a, A.act + it.m0 * F, nr * F * 2, F, it.a0, wave, lane);
+            opnd_trans(it.b, A.dy_disp + it.m0 * d, nr * d * 2, d, it.b0, wave, lane);
+        } else {                     // dW13[j][i] = sum_r dHU[r][j] X[r][i]
+            opnd_trans(it.a, A.x_disp + it.m0 * d, nr * d * 2, d, it.a0, wave, lane);
+            opnd_trans(it.b, A.dhu + it.m0 * F2, nr * F2 * 2, F2, it.b0, wave, lane);
         }
     }
+    return it;
+}
 
-    f32x16 acc[NS][2];
+template <int KIND>
+__device__ __forceinline__ void issue_bwd_stage(unsigned char *buf, int kt, const BwdItem &it,
+                                                int wave) {
+    constexpr bool BTR = !(KIND == G1_DA || KIND == G2_DX);
+    issue_opnd<BTR>(buf, it.b, kt, wave);
+    issue_opnd<true>(buf + kLdsA, it.a, kt, wave);
+}
+
+// MFMAs of one stage held in buf
+template <int KIND, int NW>
+__device__ __forceinline__ void mma_bwd_stage(const unsigned char *buf, int arow, int brow, int lane,
+                                              f32x16 (&acc)[4][2]) {
+    constexpr bool BTR = !(KIND == G1_DA || KIND == G2_DX);
+    const unsigned char *Bs = buf;
+    const unsigned char *As = buf + kLdsA;
+    bf16x8 wf[2][2], tf[2][4];
 #pragma unroll
-    for (int i = 0; i < NS; ++i)
+    for (int ks = 0; ks < BK / 16; ++ks) {
+        if (ks == 0) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s) wf[0][s] = frag<true>(As, arow + s * 32, 0, lane);
+#pragma unroll
+            for (int i = 0; i < NW; ++i) tf[0][i] = frag<BTR>(Bs, brow + i * 32, 0, lane);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (ks + 1 < BK / 16) {
+            const int n = (ks + 1) & 1;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) wf[n][s] = frag<true>(As, arow + s * 32, ks + 1, lane);
+#pragma unroll
+            for (int i = 0; i < NW; ++i) tf[n][i] = frag<BTR>(Bs, brow + i * 32, ks + 1, lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NW; ++i)
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                acc[i][s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks & 1][s], tf[ks & 1][i],
+                                                                    acc[i][s], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// One work item seen by one wave with NW (0..4) live 32-row sub-tiles of output rows.
+template <int KIND, int NW>
+__device__ __forceinline__ void run_bwd_item(unsigned char *lds, const BwdArgs &A,
+                                             const BwdItem &it, BwdItem &next, int nitem,
+                                             const int *tile_off, int t_tiles, int n_tiles,
+                                             int wave, int lane) {
+    constexpr bool DGRAD = (KIND == G1_DA || KIND == G2_DX);
+    const int d = A.d, F = A.F, F2 = 2 * F;
+    const int wn = wave & 3, wm = wave >> 2;
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < NW; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-    int brow[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) brow[s] = wave * 64 + s * 32;
+    const int arow = wn * 64, brow = wm * 128;
 
-    u32x4 rW[8], rU[8], rT[8];
-    const uint32_t ldbT = uint32_t(ldT * 2), ldbW = uint32_t(ldW * 2);
-    const int krow0 = kb * 8;                 // this thread's first row inside a stage
-    const uint32_t noffT = uint32_t((it.t0 + nb * 8) * 2);
-    const bool nokT = it.t0 + nb * 8 < nT;
-    const uint32_t noffW = uint32_t((it.n0 + nb * 8) * 2);
-    const bool nokW = it.n0 + nb * 8 < nW;
-    const char *Tbase = reinterpret_cast<const char *>(Tsrc) + it.m0 * ldT * 2;
-    const char *Wbase = reinterpret_cast<const char *>(Wsrc) + kW0 * ldW * 2;
-    auto issue = [&](int stage, int kt) {
-        unsigned char *Ts = lds + stage * (kLdsA + kLdsB);
-        if (DGRAD) {
-            const char *Tk = Tb + size_t(kt) * BK * 2;
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (j < a_groups)
-                    __builtin_amdgcn_global_load_lds(
-                        Tk + a_off[j],
-                        (__attribute__((address_space(3))) void *)(Ts + (wave * 8 + j) * 1024), 16, 0, 0);
-        } else {
-            const int kvalid = int(min<int64_t>(BK, it.m_end - it.m0 - int64_t(kt) * BK));
-            tload(rT, Tbase + size_t(kt) * BK * ldbT, ldbT, krow0, kvalid, noffT, nokT);
-        }
-        const int kvalidW = DGRAD ? BK : int(min<int64_t>(BK, k_endW - kW0 - int64_t(kt) * BK));
-        const char *Wk = Wbase + size_t(kt) * BK * ldbW;
-        tload(rW, Wk, ldbW, krow0, kvalidW, noffW, nokW);
-        if (KIND == G3_DW2) tload(rU, Wk + size_t(F) * 2, ldbW, krow0, kvalidW, noffW, nokW);
-    };
-    auto commit = [&](int stage) {
-        unsigned char *Ts = lds + stage * (kLdsA + kLdsB);
-        unsigned char *Ws = Ts + kLdsA;
-        if (KIND == G3_DW2) swiglu_rows(rW, rU);
-        tstore(rW, Ws, nb, kb);
-        if (!DGRAD) tstore(rT, Ts, nb, kb);
-    };
-
-    __syncthreads();                 // the previous item's readers are done with LDS
-    if (it.KT > 0) {
-        issue(0, 0);
-        commit(0);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-    }
+    // stage 0 was issued before the previous item's epilogue (or before the first item)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
     for (int kt = 0; kt < it.KT; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < it.KT;
-        if (more) issue(cur ^ 1, kt + 1);
-        const unsigned char *Ts = lds + cur * (kLdsA + kLdsB);
-        mma_stage<NS>(Ts, Ts + kLdsA, lane, brow, acc);
-        if (more) commit(cur ^ 1);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        unsigned char *cur = lds + (kt & 1) * (kLdsA + kLdsB);
+        if (kt + 1 < it.KT) issue_bwd_stage<KIND>(lds + ((kt + 1) & 1) * (kLdsA + kLdsB), kt + 1, it, wave);
+        if (NW > 0) mma_bwd_stage<KIND, NW>(cur, arow, brow, lane, acc);
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the next stage landed
+        __syncthreads();                 // everyone's loads landed, and cur is free
     }
 
-    // ---------------- epilogues: lane holds T-side row (lane & 31) of each 32-row
-    // sub-tile and, for v = 4g + q, W-side row 8g + 4*(lane >> 5) + q of each of its
-    // two 32-row weight sub-tiles: four consecutive outputs of one output row.
+    // every wave is past its last LDS read: the next item's first stage flies during
+    // this item's epilogue
+    if (nitem >= 0) {
+        next = make_bwd_item<KIND>(A, nitem, tile_off, t_tiles, n_tiles, wave, lane);
+        if (next.KT > 0) issue_bwd_stage<KIND>(lds, 0, next, wave);
+    }
+
+    // epilogue: lane holds output row b0 + brow + 32i + (lane & 31) and, for v = 4g + q,
+    // output column a0 + arow + 32s + 8g + 4 (lane >> 5) + q: four consecutive columns
     const int nl = 4 * (lane >> 5);
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
+    for (int i = 0; i < NW; ++i) {
         if (DGRAD) {
-            const int64_t m = it.m0 + i * 32 + (lane & 31);
+            const int64_t m = it.m0 + brow + i * 32 + (lane & 31);
             if (m >= it.m_end) continue;
 #pragma unroll
             for (int s = 0; s < 2; ++s)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const int n = it.n0 + wave * 64 + s * 32 + 8 * g + nl;
-                    if (n >= nW) continue;
+                    const int n = it.a0 + arow + s * 32 + 8 * g + nl;
                     if (KIND == G1_DA) {
+                        if (n >= F) continue;
                         const uint2 hv = *reinterpret_cast<const uint2 *>(A.hu + m * F2 + n);
                         const uint2 uv = *reinterpret_cast<const uint2 *>(A.hu + m * F2 + F + n);
                         float h[4] = {bf16_lo(hv.x), bf16_hi(hv.x), bf16_lo(hv.y), bf16_hi(hv.y)};
                         float u[4] = {bf16_lo(uv.x), bf16_hi(uv.x), bf16_lo(uv.y), bf16_hi(uv.y)};
-                        float dh[4], du[4];
+                        float dh[4], du[4], av[4];
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
                             const float da = acc[i][s][4 * g + q];
                             const float sg = 1.0f / (1.0f + __expf(-h[q]));
                             dh[q] = da * u[q] * sg * (1.0f + h[q] * (1.0f - sg));
                             du[q] = da * h[q] * sg;
+                            av[q] = silu_f(h[q]) * u[q];
                         }
-                        uint2 ph, pu;
+                        uint2 ph, pu, pa;
                         ph.x = pack_bf16x2(dh[0], dh[1]);
                         ph.y = pack_bf16x2(dh[2], dh[3]);
                         pu.x = pack_bf16x2(du[0], du[1]);
                         pu.y = pack_bf16x2(du[2], du[3]);
+                        pa.x = pack_bf16x2(av[0], av[1]);
+                        pa.y = pack_bf16x2(av[2], av[3]);
                         *reinterpret_cast<uint2 *>(A.dhu + m * F2 + n) = ph;
                         *reinterpret_cast<uint2 *>(A.dhu + m * F2 + F + n) = pu;
+                        *reinterpret_cast<uint2 *>(A.act + m * F + n) = pa;
                     } else {
+                        if (n >= d) continue;
                         uint2 p;
                         p.x = pack_bf16x2(acc[i][s][4 * g], acc[i][s][4 * g + 1]);
                         p.y = pack_bf16x2(acc[i][s][4 * g + 2], acc[i][s][4 * g + 3]);
@@ -271,16 +330,18 @@ __device__ __forceinline__ void run_bwd_item(unsigned char *lds, const BwdArgs &
                     }
                 }
         } else {
-            const int trow = it.t0 + i * 32 + (lane & 31);
-            if (trow >= nT) continue;
-            float *out = (KIND == G3_DW2) ? A.dw2 + size_t(it.e) * d * F + size_t(trow) * F
-                                          : A.dw13 + size_t(it.e) * F2 * d + size_t(trow) * d;
+            const int orow = it.b0 + brow + i * 32 + (lane & 31);
+            const int nrows = (KIND == G3_DW2) ? d : F2;
+            const int ncols = (KIND == G3_DW2) ? F : d;
+            if (orow >= nrows) continue;
+            float *out = (KIND == G3_DW2) ? A.dw2 + size_t(it.e) * d * F + size_t(orow) * F
+                                          : A.dw13 + size_t(it.e) * F2 * d + size_t(orow) * d;
 #pragma unroll
             for (int s = 0; s < 2; ++s)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const int n = it.n0 + wave * 64 + s * 32 + 8 * g + nl;
-                    if (n >= nW) continue;
+                    const int n = it.a0 + arow + s * 32 + 8 * g + nl;
+                    if (n >= ncols) continue;
                     *reinterpret_cast<float4 *>(out + n) =
                         make_float4(acc[i][s][4 * g], acc[i][s][4 * g + 1], acc[i][s][4 * g + 2],
                                     acc[i][s][4 * g + 3]);
@@ -290,8 +351,8 @@ __device__ __forceinline__ void run_bwd_item(unsigned char *lds, const BwdArgs &
 }
 
 template <int KIND>
-__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_bwd(BwdArgs A, int t_tiles, int n_tiles) {
-    extern __shared__ __align__(16) unsigned char lds[];
+__global__ __launch_bounds__(kBwdThreads) void k_gemm_bwd(BwdArgs A, int t_tiles, int n_tiles) {
+    __shared__ __align__(16) unsigned char lds[2 * (kLdsA + kLdsB)];   // two stages
     __shared__ int tile_off[kMaxE + 1];
     __shared__ int map_scratch[256];
     constexpr bool DGRAD = (KIND == G1_DA || KIND == G2_DX);
@@ -305,66 +366,41 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_bwd(BwdArgs A, int t_t
     } else {
         total = E * t_tiles * n_tiles;
     }
-    const int Kd = (KIND == G1_DA) ? A.d : 2 * A.F;
     const int G = gridDim.x;
     const int per = G / 8;
     const int slot = (G % 8 == 0) ? (blockIdx.x % 8) * per + blockIdx.x / 8 : blockIdx.x;
+    if (slot >= total) return;
+
+    BwdItem it = make_bwd_item<KIND>(A, slot, tile_off, t_tiles, n_tiles, wave, lane);
+    if (it.KT > 0) issue_bwd_stage<KIND>(lds, 0, it, wave);
     for (int base = 0; base < total; base += G) {
         // rotating the slot each round spreads large and small items evenly
-        const int item = base + (slot + base / G) % G;
-        if (item >= total) break;
-        BwdItem it;
+        const int nbase = base + G;
+        const int nitem = nbase + (slot + nbase / G) % G;
+        const bool has_next = nitem < total;
+        BwdItem next;
+        // live 32-row sub-tiles of output rows in this wave's half
         int nsub;
-        if (DGRAD) {
-            const ItemCoord ic = decode_item(item, tile_off, E, n_tiles);
-            it.e = ic.e;
-            it.m0 = int64_t(A.expert_off[ic.e]) + int64_t(ic.mt) * BM;
-            it.m_end = min<int64_t>(A.expert_off[ic.e + 1], A.rows_alloc);
-            it.t0 = 0;
-            it.n0 = ic.nt * BNW;
-            it.KT = Kd / BK;
-            nsub = int(min<int64_t>(8, (it.m_end - it.m0 + 31) / 32));
-        } else {
-            it.e = item / (t_tiles * n_tiles);
-            const int rem = item % (t_tiles * n_tiles);
-            const int tt = rem / n_tiles, nt = rem % n_tiles;
-            it.m0 = min<int64_t>(A.expert_off[it.e], A.rows_alloc);
-            it.m_end = max(it.m0, min<int64_t>(A.expert_off[it.e + 1], A.rows_alloc));
-            it.t0 = tt * BM;
-            it.n0 = nt * BNW;
-            it.KT = int((it.m_end - it.m0 + BK - 1) / BK);
-            const int nT = (KIND == G3_DW2) ? A.d : 2 * A.F;
-            nsub = min(8, (nT - it.t0 + 31) / 32);
+        if (DGRAD) nsub = int(min<int64_t>(8, (it.m_end - it.m0 + 31) / 32));
+        else nsub = min(8, (((KIND == G3_DW2) ? A.d : 2 * A.F) - it.b0 + 31) / 32);
+        const int nw = min(4, max(0, nsub - (wave >> 2) * 4));
+        switch (nw) {
+        case 4: run_bwd_item<KIND, 4>(lds, A, it, next, has_next ? nitem : -1, tile_off, t_tiles, n_tiles, wave, lane); break;
+        case 3: run_bwd_item<KIND, 3>(lds, A, it, next, has_next ? nitem : -1, tile_off, t_tiles, n_tiles, wave, lane); break;
+        case 2: run_bwd_item<KIND, 2>(lds, A, it, next, has_next ? nitem : -1, tile_off, t_tiles, n_tiles, wave, lane); break;
+        case 1: run_bwd_item<KIND, 1>(lds, A, it, next, has_next ? nitem : -1, tile_off, t_tiles, n_tiles, wave, lane); break;
+        default: run_bwd_item<KIND, 0>(lds, A, it, next, has_next ? nitem : -1, tile_off, t_tiles, n_tiles, wave, lane); break;
         }
-        switch (nsub) {
-        case 8: run_bwd_item<KIND, 8>(lds, A, it, wave, lane); break;
-        case 7: run_bwd_item<KIND, 7>(lds, A, it, wave, lane); break;
-        case 6: run_bwd_item<KIND, 6>(lds, A, it, wave, lane); break;
-        case 5: run_bwd_item<KIND, 5>(lds, A, it, wave, lane); break;
-        case 4: run_bwd_item<KIND, 4>(lds, A, it, wave, lane); break;
-        case 3: run_bwd_item<KIND, 3>(lds, A, it, wave, lane); break;
-        case 2: run_bwd_item<KIND, 2>(lds, A, it, wave, lane); break;
-        default: run_bwd_item<KIND, 1>(lds, A, it, wave, lane); break;
-        }
+        if (!has_next) break;
+        it = next;
     }
 }
 
-bool set_bwd_lds_limits() {
-    static int ok = -1;
-    if (ok < 0) {
-        ok = 1;
-        const void *fns[4] = {reinterpret_cast<const void *>(&k_gemm_bwd<G1_DA>),
-                              reinterpret_cast<const void *>(&k_gemm_bwd<G2_DX>),
-                              reinterpret_cast<const void *>(&k_gemm_bwd<G3_DW2>),
-                              reinterpret_cast<const void *>(&k_gemm_bwd<G4_DW13>)};
-        for (const void *f : fns)
-            if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsGemm) != hipSuccess)
-                ok = 0;
-    }
-    return ok == 1;
+// Workspace: dHU [rows, 2F] then a [rows, F], both bf16.
+size_t bwd_dhu_bytes(int64_t rows, int64_t F) { return align256(size_t(rows) * 2 * F * 2); }
+size_t bwd_ws_bytes(int64_t rows, int64_t F) {
+    return bwd_dhu_bytes(rows, F) + align256(size_t(rows) * F * 2);
 }
-
-size_t bwd_ws_bytes(int64_t rows, int64_t F) { return align256(size_t(rows) * 2 * F * 2); }
 
 }  // namespace
 }  // namespace moe
@@ -386,7 +422,7 @@ extern "C" moe_status_t moe_expert_ffn_bwd(const void *x_disp, const void *dy_di
     if (!valid_dtype(dtype) || E <= 0 || rows < 0 || d <= 0 || F <= 0) return MOE_ERR_INVALID_ARG;
     if (dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
     if (E > kMaxE || rows >= (int64_t(1) << 31) || d % BK != 0 || F % BK != 0 || d > (1 << 20) ||
-        F > (1 << 20) || int64_t(d) * 2 * F >= (int64_t(1) << 31))
+        F > (1 << 20) || int64_t(d) * 2 * F * 2 >= (int64_t(1) << 31))
         return MOE_ERR_UNSUPPORTED;
     if (!x_disp || !dy_disp || !hu_save || !expert_off || !w13 || !w2 || !dx_disp || !dw13 || !dw2 ||
         !ws)
@@ -396,7 +432,6 @@ extern "C" moe_status_t moe_expert_ffn_bwd(const void *x_disp, const void *dy_di
     if (!aligned16(x_disp) || !aligned16(dy_disp) || !aligned16(hu_save) || !aligned16(w13) ||
         !aligned16(w2) || !aligned16(dx_disp) || !aligned16(dw13) || !aligned16(dw2))
         return MOE_ERR_ALIGN;
-    if (!set_bwd_lds_limits()) return MOE_ERR_HIP;     // first HIP call: all checks done
     const hipStream_t st = as_stream(stream);
     BwdArgs A;
     A.x_disp = static_cast<const uint16_t *>(x_disp);
@@ -406,6 +441,7 @@ extern "C" moe_status_t moe_expert_ffn_bwd(const void *x_disp, const void *dy_di
     A.w2 = static_cast<const uint16_t *>(w2);
     A.expert_off = expert_off;
     A.dhu = static_cast<uint16_t *>(ws);
+    A.act = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + bwd_dhu_bytes(rows, F));
     A.dx_disp = static_cast<uint16_t *>(dx_disp);
     A.dw13 = dw13;
     A.dw2 = dw2;
@@ -422,23 +458,23 @@ extern "C" moe_status_t moe_expert_ffn_bwd(const void *x_disp, const void *dy_di
         const int nt = int(cdiv(F, BNW));
         const int g = int(std::min<int64_t>(max_mt * nt, cus));
         if (g > 0)
-            hipLaunchKernelGGL(k_gemm_bwd<G1_DA>, dim3(g), dim3(kGemmThreads), kLdsGemm, st, A, 0, nt);
+            hipLaunchKernelGGL(k_gemm_bwd<G1_DA>, dim3(g), dim3(kBwdThreads), 0, st, A, 0, nt);
     }
     {   // G3: dW2 (independent of G1)
         const int tt = int(cdiv(d, BM)), nt = int(cdiv(F, BNW));
         const int g = int(std::min<int64_t>(int64_t(E) * tt * nt, cus));
-        hipLaunchKernelGGL(k_gemm_bwd<G3_DW2>, dim3(g), dim3(kGemmThreads), kLdsGemm, st, A, tt, nt);
+        hipLaunchKernelGGL(k_gemm_bwd<G3_DW2>, dim3(g), dim3(kBwdThreads), 0, st, A, tt, nt);
     }
     {   // G2: dX
         const int nt = int(cdiv(d, BNW));
         const int g = int(std::min<int64_t>(max_mt * nt, cus));
         if (g > 0)
-            hipLaunchKernelGGL(k_gemm_bwd<G2_DX>, dim3(g), dim3(kGemmThreads), kLdsGemm, st, A, 0, nt);
+            hipLaunchKernelGGL(k_gemm_bwd<G2_DX>, dim3(g), dim3(kBwdThreads), 0, st, A, 0, nt);
     }
     {   // G4: dW13
         const int tt = int(cdiv(2 * F, BM)), nt = int(cdiv(d, BNW));
         const int g = int(std::min<int64_t>(int64_t(E) * tt * nt, cus));
-        hipLaunchKernelGGL(k_gemm_bwd<G4_DW13>, dim3(g), dim3(kGemmThreads), kLdsGemm, st, A, tt, nt);
+        hipLaunchKernelGGL(k_gemm_bwd<G4_DW13>, dim3(g), dim3(kBwdThreads), 0, st, A, tt, nt);
     }
     return launch_status();
 }
