@@ -193,11 +193,18 @@ moe_status_t moe_combine(const void *y_disp, const int32_t *pair_slot, const flo
  *                   dA = dO W2;  dh = dA * u * s * (1 + h (1 - s)), s = sigmoid(h);
  *                   du = dA * silu(h);  dX = dh W1 + du W3      -> dx_disp (dtype)
  *                   dW2 = dO^T a;  dW1 = dh^T X;  dW3 = du^T X  -> dw2, dw13 (f32)
- * moe_route_bwd:    dlogits_sel[t,j] = g_j (dg_j - sum_i g_i dg_i)   (f32, RENORM gating)
+ *                   a = silu(h) * u is recomputed from hu_save. ws: at least
+ *                   moe_expert_ffn_bwd_workspace_size() bytes, 256-byte aligned (it
+ *                   holds [dh du] and a in bf16; contents undefined afterwards).
+ *                   d and F multiples of 64, 2F * d * 2 bytes < 2^31, E <= 1024;
+ *                   otherwise MOE_ERR_UNSUPPORTED. Every dw13/dw2 entry is written,
+ *                   zeros for experts without rows.
+ * moe_route_bwd:   dlogits_sel[t,j] = g_j (dg_j - sum_i g_i dg_i)   (f32, RENORM gating)
  *                   dw_router[e,:] = sum over the rows of expert e in the expert-major
  *                                    plan (expert_off, row_pair from moe_dispatch),
- *                                    i.e. its tokens in ascending order, of
- *                                    dlogits_sel[t,j] * x[t,:]      (f32)
+ *                                    i.e. over its tokens, of
+ *                                    dlogits_sel[t,j] * x[t,:]      (f32, summed in
+ *                                    one fixed order: bitwise reproducible)
  * moe_dispatch_bwd: dx[t] = sum_j dx_disp[pair_slot[t,j]]
  *                           + sum_j dlogits_sel[t,j] * w_router[topk_idx[t,j]]
  *                   (second term skipped if dlogits_sel is NULL), float32 sum in
