@@ -32,6 +32,10 @@ trillion-parameter models on AWS EFA" (N. Licker, K. Hu, V. Zaytsev, L. Chen,
                   gate weights: y[t] = sum_j g[t,j] o[slot(t,j)], accumulated at the
                   receiver ([EFA] Introduction; Dispatch and combine; Dispatch/combine
                   latency).
+* receive order   a destination's region (one chunk per sender) reordered so that each
+                  local expert's rows are contiguous before its grouped GEMM ([EFA]
+                  Dispatch and combine, receiver side); senders ascending inside an
+                  expert (a stable reading: the pages leave the order open).
 * backward        the transposes of the above, and the softmax-over-top-k Jacobian.
 
 Precision: everything is float64 except the router logits, which decide integers and
@@ -200,6 +204,42 @@ def plan(idx, E: int, n_src: int = 1, n_dst: int = 1, cap_rows_per_dst: int | No
             row_pair[row] = t * k + j
     return {"counts": counts, "expert_off": expert_off, "chunk_off": chunk_off,
             "pair_slot": pair_slot, "row_pair": row_pair, "cap": cap}
+
+
+# ------------------------------------------------------ receive side (emulated EP)
+def ep_recv_plan(counts, chunk_off, r: int, n_dst: int, cap: int):
+    """Destination r's receive region in expert-major order.
+
+    [EFA] Dispatch and combine: the receiver moves the tokens it got into the tensor
+    the grouped GEMM consumes; [EFA] Send and receive buffers: each sender's rows sit
+    in one contiguous chunk of the destination's region. Inside sender s's chunk
+    (at chunk_off[r, s]) the rows of the destination's experts follow each other in
+    ascending expert id, each block in the sender's own (ascending token) order, as
+    written by plan(). The local order lists local expert le = e - r*epr ascending,
+    inside it the senders ascending, inside those the sender's order.
+
+    Returns local_off [epr+1] (exclusive cumulative sum of the local experts' row
+    totals) and row_src [cap]: for local row j < local_off[epr], the row of the
+    region (0-based inside destination r) it comes from; -1 for the rest.
+    """
+    counts = np.asarray(counts, dtype=np.int64)
+    chunk_off = np.asarray(chunk_off, dtype=np.int64)
+    n_src, E = counts.shape
+    epr = E // n_dst
+    local_off = np.zeros(epr + 1, dtype=np.int64)
+    row_src = []
+    for le in range(epr):
+        e = r * epr + le
+        for s in range(n_src):
+            # rows of sender s for expert e: after its rows for the lower local experts
+            start = chunk_off[r, s] + counts[s, r * epr:e].sum()
+            for i in range(counts[s, e]):
+                row_src.append(int(start + i))
+        local_off[le + 1] = len(row_src)
+    assert len(row_src) <= cap
+    out = np.full(cap, -1, dtype=np.int64)
+    out[:len(row_src)] = row_src
+    return local_off, out
 
 
 # ----------------------------------------------------------------------- dispatch

@@ -133,3 +133,49 @@ def test_dispatch_copies_rows_bitwise():
             assert np.array_equal(xd[p["pair_slot"][t, j]].view(np.uint32), x[t].view(np.uint32))
     # every row is filled by exactly the token row_pair names
     assert np.array_equal(xd, x[p["row_pair"] // k])
+
+
+# ------------------------------------------------------------ receive side (EP)
+def test_ep_recv_plan_golden():
+    """The hand-worked receive order of the 2-sender, 2-destination example."""
+    case = json.load(open(os.path.join(GOLDEN, "plan_examples.json")))["cases"][1]
+    p = oracle.plan(np.array(case["idx"]), case["E"], case["n_src"], case["n_dst"], case["cap"])
+    for r in range(case["n_dst"]):
+        off, src = oracle.ep_recv_plan(p["counts"], p["chunk_off"], r, case["n_dst"], case["cap"])
+        assert off.tolist() == case["ep_recv"]["local_off"][r]
+        assert src.tolist() == case["ep_recv"]["row_src"][r]
+
+
+@pytest.mark.parametrize("T,E,k", [(40, 8, 2), (257, 16, 5)])
+def test_ep_recv_plan_single_rank_is_identity(T, E, k):
+    """One sender, one destination: the region already is expert-major."""
+    rng = np.random.default_rng(T)
+    idx = _random_idx(rng, T, E, k)
+    p = oracle.plan(idx, E)
+    off, src = oracle.ep_recv_plan(p["counts"], p["chunk_off"], 0, 1, p["cap"])
+    assert np.array_equal(off, p["expert_off"])
+    assert np.array_equal(src, np.arange(T * k))
+
+
+def test_ep_recv_plan_matches_expert_major_layout():
+    """At the 32 x 128 Zipf workload, every destination's reordered region holds
+    exactly the pairs of its experts in the order of the plain expert-major layout
+    (which plan() builds independently), and its live rows are a permutation of
+    the region's live rows."""
+    wl = moe_synth.WORKLOADS["ep32_zipf"]
+    idx, _ = moe_synth.zipf_routing(wl)
+    idx = np.asarray(idx)
+    p_ep = oracle.plan(idx, wl.E, wl.n_src, wl.n_dst, wl.cap_rows_per_dst)
+    p_em = oracle.plan(idx, wl.E)
+    cap, epr = p_ep["cap"], wl.E // wl.n_dst
+    em_pair_of_row = p_em["row_pair"]
+    for r in range(wl.n_dst):
+        off, src = oracle.ep_recv_plan(p_ep["counts"], p_ep["chunk_off"], r, wl.n_dst, cap)
+        live = int(p_ep["chunk_off"][r, wl.n_src])
+        assert off[-1] == live
+        assert np.array_equal(np.sort(src[:live]), np.arange(live))
+        assert np.all(src[live:] == -1)
+        lo, hi = p_em["expert_off"][r * epr], p_em["expert_off"][(r + 1) * epr]
+        assert np.array_equal(off, p_em["expert_off"][r * epr:(r + 1) * epr + 1] - lo)
+        pairs_local = p_ep["row_pair"][r * cap + src[:live]]
+        assert np.array_equal(pairs_local, em_pair_of_row[lo:hi])
