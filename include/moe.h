@@ -182,6 +182,35 @@ moe_status_t moe_combine(const void *y_disp, const int32_t *pair_slot, const flo
                          int64_t T, int32_t k, int64_t d, int64_t rows_total, moe_dtype_t dtype,
                          void *y, void *stream);
 
+/* ------------------------------------------- receive side of the rank-major layout
+ * [EFA] Dispatch and combine: the receiver moves the tokens it got into the tensor
+ * handed to the grouped GEMM; [EFA] Send and receive buffers: destination r's region
+ * holds one contiguous chunk per sender. These calls give one destination its
+ * expert-major input and return the expert outputs to the region for combine.
+ *
+ * moe_ep_recv_plan: from the plan of a rank-major moe_dispatch (counts [n_src,E],
+ *   chunk_off [n_dst, n_src+1]; E/n_dst = epr local experts), destination r's order:
+ *   local expert le = e - r*epr ascending, inside it senders ascending, inside those
+ *   the sender's own (ascending token) order.
+ *     local_off [epr+1]  exclusive cumulative sum of the local experts' rows
+ *     row_src   [cap]    region row (0-based inside r's region) of local row j for
+ *                        j < local_off[epr]; -1 for the rest
+ *   Limits: epr <= 1024, epr * n_src <= 8192, cap < 2^31. A plan the dispatch
+ *   flagged over capacity is cut at cap.
+ * moe_ep_recv_gather:  x_local[j]  = x_region[row_src[j]]  (bit copy, rows with -1
+ *                      untouched); x_region = x_disp + r*cap rows.
+ * moe_ep_recv_scatter: y_region[row_src[j]] = y_local[j]   (bit copy).
+ * Between the two, moe_expert_ffn(x_local, local_off, w13 + r*epr experts, w2 + ...,
+ * epr, rows = cap, ...) is destination r's grouped GEMM; combine then runs at the
+ * sources on the whole rank-major y_disp with the dispatch's pair_slot. */
+moe_status_t moe_ep_recv_plan(const int32_t *counts, const int32_t *chunk_off, int32_t n_src,
+                              int32_t n_dst, int32_t E, int32_t r, int64_t cap,
+                              int32_t *local_off, int32_t *row_src, void *stream);
+moe_status_t moe_ep_recv_gather(const void *x_region, const int32_t *row_src, int64_t cap,
+                                int64_t d, moe_dtype_t dtype, void *x_local, void *stream);
+moe_status_t moe_ep_recv_scatter(const void *y_local, const int32_t *row_src, int64_t cap,
+                                 int64_t d, moe_dtype_t dtype, void *y_region, void *stream);
+
 /* ---------------------------------------------------------------- backward
  * The transposes of the steps above (the layer's gradient; the article covers
  * only the forward data movement).

@@ -105,3 +105,18 @@ def test_ffn_combine_bwd_host_validation(lib):
     assert cb(FAKE, FAKE, FAKE, FAKE, 10, 40, 64, 20, BF16, FAKE, FAKE, None) == UNSUPPORTED
     db = lib.moe_dispatch_bwd
     assert db(FAKE, FAKE, None, FAKE, None, 10, 2, 64, 8, 20, BF16, FAKE, None) == INVALID
+
+
+def test_ep_recv_host_validation(lib):
+    p = lib.moe_ep_recv_plan
+    assert p(FAKE, FAKE, 32, 32, 384, 32, 49152, FAKE, FAKE, None) == SHAPE      # r >= n_dst
+    assert p(FAKE, FAKE, 32, 5, 384, 0, 49152, FAKE, FAKE, None) == SHAPE       # E % n_dst
+    assert p(FAKE, FAKE, 64, 1, 1024, 0, 100, FAKE, FAKE, None) == UNSUPPORTED  # epr*n_src
+    assert p(None, FAKE, 32, 32, 384, 0, 49152, FAKE, FAKE, None) == INVALID
+    assert p(FAKE, FAKE, 0, 32, 384, 0, 49152, FAKE, FAKE, None) == INVALID
+    g, s = lib.moe_ep_recv_gather, lib.moe_ep_recv_scatter
+    assert g(FAKE, FAKE, 100, 60, BF16, FAKE, None) == ALIGN                    # 120-byte rows
+    assert g(FAKE + 8, FAKE, 100, 64, BF16, FAKE, None) == ALIGN
+    assert s(FAKE, None, 100, 64, BF16, FAKE, None) == INVALID
+    assert s(None, None, 0, 64, BF16, None, None) == OK                         # nothing to do
+    assert g(FAKE, FAKE, 1 << 31, 64, BF16, FAKE, None) == UNSUPPORTED

@@ -20,7 +20,8 @@ import torch
 __all__ = ["MoEError", "load", "library_path", "moe_abi_version", "moe_route", "moe_dispatch",
            "moe_dispatch_status", "moe_expert_ffn", "moe_expert_ffn_gate_up",
            "moe_expert_ffn_down", "moe_combine", "moe_combine_bwd",
-           "moe_expert_ffn_bwd", "moe_route_bwd", "moe_dispatch_bwd", "Layout", "forward",
+           "moe_expert_ffn_bwd", "moe_route_bwd", "moe_dispatch_bwd", "moe_ep_recv_plan",
+           "moe_ep_recv_gather", "moe_ep_recv_scatter", "Layout", "forward",
            "backward",
            "EXPORTED"]
 
@@ -57,6 +58,9 @@ EXPORTED = {
     "moe_route_bwd": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _P, _P, _P]),
     "moe_dispatch_bwd": (_I32, [_P, _P, _P, _P, _P, _I64, _I32, _I64, _I32, _I64, _I32, _P,
                                 _P]),
+    "moe_ep_recv_plan": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I64, _P, _P, _P]),
+    "moe_ep_recv_gather": (_I32, [_P, _P, _I64, _I64, _I32, _P, _P]),
+    "moe_ep_recv_scatter": (_I32, [_P, _P, _I64, _I64, _I32, _P, _P]),
 }
 
 
@@ -301,6 +305,42 @@ def moe_dispatch_bwd(dx_disp, pair_slot, *, topk_idx=None, dlogits_sel=None, w_r
         _ptr(dx_disp), _ptr(pair_slot), _ptr(topk_idx), _ptr(dlogits_sel), _ptr(w_router), T, k,
         d, E, rows, _dt(dx_disp), _ptr(dx), _stream(stream)))
     return dx
+
+
+# ------------------------------------------------- receive side (rank-major layout)
+def moe_ep_recv_plan(counts, chunk_off, r: int, cap: int, *, local_off=None, row_src=None,
+                     stream=None):
+    """Destination r's expert-major order of its region: (local_off [E/n_dst+1],
+    row_src [cap]) from a rank-major dispatch plan's counts and chunk_off."""
+    n_src, E = counts.shape
+    n_dst = chunk_off.shape[0]
+    dev = counts.device
+    if local_off is None:
+        local_off = torch.empty(E // n_dst + 1, dtype=torch.int32, device=dev)
+    if row_src is None:
+        row_src = torch.empty(cap, dtype=torch.int32, device=dev)
+    _check("moe_ep_recv_plan", load().moe_ep_recv_plan(
+        _ptr(counts), _ptr(chunk_off), n_src, n_dst, E, r, cap, _ptr(local_off), _ptr(row_src),
+        _stream(stream)))
+    return local_off, row_src
+
+
+def moe_ep_recv_gather(x_region, row_src, *, x_local=None, stream=None):
+    """x_local[j] = x_region[row_src[j]] for the live rows (the rest untouched)."""
+    cap, d = x_region.shape
+    if x_local is None:
+        x_local = torch.empty_like(x_region)
+    _check("moe_ep_recv_gather", load().moe_ep_recv_gather(
+        _ptr(x_region), _ptr(row_src), cap, d, _dt(x_region), _ptr(x_local), _stream(stream)))
+    return x_local
+
+
+def moe_ep_recv_scatter(y_local, row_src, y_region, *, stream=None):
+    """y_region[row_src[j]] = y_local[j] for the live rows."""
+    cap, d = y_local.shape
+    _check("moe_ep_recv_scatter", load().moe_ep_recv_scatter(
+        _ptr(y_local), _ptr(row_src), cap, d, _dt(y_local), _ptr(y_region), _stream(stream)))
+    return y_region
 
 
 # ------------------------------------------------------------ whole layer
