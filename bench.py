@@ -8,7 +8,8 @@ E=64, k=6, F=1408 bf16 layer. The same JSON line also reports:
   train_step   forward + backward of that layer (combine_bwd, expert_ffn_bwd,
                route_bwd, dispatch_bwd) on the same shapes,
   ep_dispatch_combine  the rank-major dispatch and combine of 32 source ranks x 128
-               tokens, d=7168, E=384, k=8, Zipf(1.2) routing (identity experts),
+               tokens, d=7168, E=384, k=8, Zipf(1.2) routing (identity experts), and
+               destination 0's receive path (reorder, 12-expert SwiGLU GEMM, scatter),
   large        the T=8192, d=7168, E=384, k=8, F=2048 layer forward (34 GB weights),
   roofline     the dominant kernel of the headline step, timed live with HIP events,
   cpu_baseline the CPU oracle on the host cores over whole passes of the headline
@@ -46,6 +47,8 @@ def parse():
     ap.add_argument("--no-large", action="store_true", help="skip the 34 GB large-layer run")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--only-ep", action="store_true",
+                    help="run only the rank-major dispatch/combine and receive path")
     ap.add_argument("--only-train", action="store_true",
                     help="run only the forward + backward step (for profiler runs)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -245,9 +248,57 @@ def ep_bench(torch, moe, wl, dev, steps, warmup):
                        f"{wl.tokens_per_src} tokens, d={wl.d} E={wl.E} k={wl.k}, Zipf({wl.zipf_s}), "
                        f"{wl.cap_rows_per_dst} rows per destination",
            "max_rows_per_dst": int(live.max()), "stages": stages}
+    out["receive_rank0"] = ep_receive_bench(torch, moe, wl, plan, steps, warmup)
     del plan, x
     torch.cuda.empty_cache()
     return out
+
+
+def ep_receive_bench(torch, moe, wl, plan, steps, warmup, r=0, F=2048):
+    """Destination r's receive path on the rank-major plan: its expert-major order,
+    the gather, its grouped GEMM on the E/n_dst local experts (SwiGLU, F=2048, random
+    weights), and the scatter back into its region."""
+    cap, epr, d = wl.cap_rows_per_dst, wl.E // wl.n_dst, wl.d
+    dev = plan["x_disp"].device
+    region = plan["x_disp"][r * cap:(r + 1) * cap]
+    g = torch.Generator(device=dev).manual_seed(7)
+    w13 = (torch.randn((epr, 2 * F, d), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    w2 = (torch.randn((epr, d, F), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    off, src = moe.moe_ep_recv_plan(plan["counts"], plan["chunk_off"], r, cap)
+    x_local = torch.empty_like(region)
+    act = torch.empty((cap, F), dtype=torch.bfloat16, device=dev)
+    y_local = torch.empty_like(region)
+    y_region = torch.empty_like(region)
+
+    def step(ev):
+        ev[0].record()
+        moe.moe_ep_recv_plan(plan["counts"], plan["chunk_off"], r, cap, local_off=off, row_src=src)
+        ev[1].record()
+        moe.moe_ep_recv_gather(region, src, x_local=x_local)
+        ev[2].record()
+        moe.moe_expert_ffn_gate_up(x_local, off, w13, act=act)
+        ev[3].record()
+        moe.moe_expert_ffn_down(act, off, w2, y_disp=y_local)
+        ev[4].record()
+        moe.moe_ep_recv_scatter(y_local, src, y_region)
+        ev[5].record()
+
+    elapsed, events = timed(torch, step, 5, steps, warmup)
+    L = int(off[-1])
+    b = 2
+    work = {"recv_plan": dict(bytes=wl.n_src * epr * 4 + cap * 4, flops=0, unit="hbm"),
+            "gather": dict(bytes=2 * L * d * b, flops=0, unit="hbm"),
+            "gate_up": dict(bytes=epr * 2 * F * d * b + L * d * b + L * F * b,
+                            flops=2 * L * d * 2 * F, unit="mfma"),
+            "down": dict(bytes=epr * d * F * b + L * F * b + L * d * b, flops=2 * L * F * d,
+                         unit="mfma"),
+            "scatter": dict(bytes=2 * L * d * b, flops=0, unit="hbm")}
+    stages = summarize(["recv_plan", "gather", "gate_up", "down", "scatter"], events, steps, work)
+    res = {"workload": f"destination {r} of {wl.n_dst}: {L} rows over {epr} local experts, "
+                       f"SwiGLU F={F} (random weights)",
+           "rows": L, "ms": round(elapsed / steps * 1e3, 4), "stages": stages}
+    del w13, w2, x_local, act, y_local, y_region
+    return res
 
 
 def cpu_baseline(wl, inp, target_s):
@@ -326,6 +377,10 @@ def main():
     moe.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only_ep:
+        ep = ep_bench(torch, moe, moe_synth.WORKLOADS["ep32_zipf"], dev, args.steps, args.warmup)
+        print(json.dumps({"ep_dispatch_combine": ep}), flush=True)
+        return
     if args.only_train:
         ts = train_bench(torch, moe, moe_synth.WORKLOADS["mid_bf16_train"], dev, args.steps,
                          args.warmup)
