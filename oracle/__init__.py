@@ -206,6 +206,76 @@ def plan(idx, E: int, n_src: int = 1, n_dst: int = 1, cap_rows_per_dst: int | No
             "pair_slot": pair_slot, "row_pair": row_pair, "cap": cap}
 
 
+# ------------------------------------------------- block-scaled fp8 dispatch payload
+# [EFA] evaluation: dispatch carries block-scaled fp8, combine stays bf16. The pages do
+# not fix the format; reading used: OCP FP8 E4M3 (1 sign, 4 exponent bits with bias 7,
+# 3 mantissa bits; largest finite value 448, no infinities, S.1111.111 is NaN), blocks
+# of 128 consecutive hidden elements of a row, one float32 scale per block equal to the
+# block's largest magnitude over 448, codes = E4M3(x * (448 / largest magnitude)) (the
+# reciprocal rounded to float32 once per block, the product once per element) rounded
+# to nearest even and saturated at +-448; an all-zero block has scale 0 and zero codes.
+E4M3_MAX = 448.0
+FP8_BLOCK = 128
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Value of each E4M3 code, straight from the field definitions (float32)."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    val = np.where((e == 15) & (m == 7), np.nan, val)
+    return (sign * val).astype(np.float32)
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """float32 values -> E4M3 codes, round to nearest even, saturating at +-448.
+    Exact: for float32 inputs every step below is exact in float64."""
+    v = np.asarray(v, dtype=np.float32).astype(np.float64)
+    sgn = np.where(np.signbit(v), 0x80, 0).astype(np.int64)
+    a = np.abs(v)
+    # subnormal range [0, 2^-6): steps of 2^-9; a rounded 8 is the first normal code
+    sub = np.rint(a * 2.0 ** 9).astype(np.int64)
+    # normal range: a = f * 2^ex with f in [0.5, 1), so a = (2f) * 2^(ex-1), 2f in [1, 2)
+    f, ex = np.frexp(a)
+    e = ex.astype(np.int64) - 1
+    q = np.rint((2.0 * f - 1.0) * 8.0).astype(np.int64)
+    carry = q == 8
+    e = np.where(carry, e + 1, e)
+    q = np.where(carry, 0, q)
+    nrm = np.minimum(((e + 7) << 3) | q, 0x7E)
+    code = np.where(a < 2.0 ** -6, sub, nrm)
+    code = np.where(a >= E4M3_MAX, 0x7E, code)
+    return (sgn | code).astype(np.uint8)
+
+
+def quantize_blocks_fp8(x, block: int = FP8_BLOCK):
+    """Per row, per block of `block` elements with m = max|x|: scale = m / 448 and
+    codes = E4M3(x * (448 / m)), every operation in float32 with one rounding.
+    Returns (codes uint8 [T,d], scales f32 [T,d/block])."""
+    x = _f32(x)
+    T, d = x.shape
+    assert d % block == 0
+    xb = x.reshape(T, d // block, block)
+    amax = np.abs(xb).max(axis=2).astype(np.float32)
+    scales = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    safe = np.where(amax > 0, amax, np.float32(1.0)).astype(np.float32)
+    inv = (np.float32(E4M3_MAX) / safe).astype(np.float32)
+    ratio = (xb * inv[:, :, None]).astype(np.float32)
+    codes = e4m3_encode(ratio)
+    codes[amax == 0] = 0
+    return codes.reshape(T, d), scales
+
+
+def dequantize_blocks_fp8(codes, scales, block: int = FP8_BLOCK) -> np.ndarray:
+    """value = decode(code) * scale, in float32 (one rounding)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    T, d = codes.shape
+    vals = e4m3_decode(codes).reshape(T, d // block, block)
+    return (vals * np.asarray(scales, dtype=np.float32)[:, :, None]).astype(np.float32).reshape(T, d)
+
+
 # ------------------------------------------------------ receive side (emulated EP)
 def ep_recv_plan(counts, chunk_off, r: int, n_dst: int, cap: int):
     """Destination r's receive region in expert-major order.
