@@ -249,9 +249,41 @@ def ep_bench(torch, moe, wl, dev, steps, warmup):
                        f"{wl.cap_rows_per_dst} rows per destination",
            "max_rows_per_dst": int(live.max()), "stages": stages}
     out["receive_rank0"] = ep_receive_bench(torch, moe, wl, plan, steps, warmup)
+    out["fp8"] = ep_fp8_bench(torch, moe, wl, x, idx, plan, lay, steps, warmup)
     del plan, x
     torch.cuda.empty_cache()
     return out
+
+
+def ep_fp8_bench(torch, moe, wl, x, idx, plan, lay, steps, warmup, r=0):
+    """The same dispatch with a block-scaled fp8 payload (E4M3 + one f32 scale per 128
+    elements), and destination r's dequantizing reorder into its expert-major bf16
+    input."""
+    cap, d = wl.cap_rows_per_dst, wl.d
+    q = moe.moe_dispatch_fp8(x, idx, wl.E, layout=lay)
+    off, src = moe.moe_ep_recv_plan(q["counts"], q["chunk_off"], r, cap)
+    x_local = torch.empty((cap, d), dtype=torch.bfloat16, device=x.device)
+
+    def step(ev):
+        ev[0].record()
+        moe.moe_dispatch_fp8(x, idx, wl.E, layout=lay, out=q)
+        ev[1].record()
+        moe.moe_ep_recv_gather_fp8(q["q_disp"][r * cap:(r + 1) * cap],
+                                   q["q_scale"][r * cap:(r + 1) * cap], src, x_local=x_local)
+        ev[2].record()
+
+    elapsed, events = timed(torch, step, 2, steps, warmup)
+    if moe.moe_dispatch_status(q["ws"]) != 0:
+        raise RuntimeError("fp8 dispatch raised its device flag")
+    P, L = wl.T * wl.k, int(off[-1])
+    row_q = d + d // 128 * 4
+    work = {"dispatch_fp8": dict(bytes=wl.T * d * 2 + P * row_q, flops=0, unit="hbm"),
+            "dequant_gather": dict(bytes=L * row_q + L * d * 2, flops=0, unit="hbm")}
+    stages = summarize(["dispatch_fp8", "dequant_gather"], events, steps, work)
+    res = {"payload_bytes_per_row": row_q, "bf16_bytes_per_row": 2 * d,
+           "dequant_rows": L, "stages": stages}
+    del q, x_local
+    return res
 
 
 def ep_receive_bench(torch, moe, wl, plan, steps, warmup, r=0, F=2048):

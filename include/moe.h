@@ -139,6 +139,23 @@ moe_status_t moe_dispatch(const void *x, const int32_t *topk_idx, int64_t T, int
  * from the flag the last moe_dispatch on `ws` raised. */
 moe_status_t moe_dispatch_status(const void *ws, void *stream);
 
+/* moe_dispatch_fp8: the same plan, with the rows sent as block-scaled fp8 ([EFA]
+ * evaluation: dispatch in block-scaled fp8, combine in bf16; the format is not on the
+ * pages, this is the reading taken). x is bf16 [T,d] with d % 128 == 0. For every
+ * row r and 128-element block b of its token, with m = max |x| over the block:
+ *   q_scale[r, b]  = m / 448                                         (f32)
+ *   q_disp[r, i]   = E4M3(x[t,i] * (448 / m)), round to nearest even, saturating at
+ *                    +-448 (OCP FP8 E4M3: bias 7, 3 mantissa bits); 0 codes, scale 0
+ *                    for an all-zero block. Every f32 operation rounds once.
+ * q_disp [rows, d] uint8 (16-byte aligned), q_scale [rows, d/128] f32 (16-byte
+ * aligned), rows = n_dst * cap; unused rows are not written. Other arguments, the
+ * plan outputs, limits and errors as for moe_dispatch. */
+moe_status_t moe_dispatch_fp8(const void *x, const int32_t *topk_idx, int64_t T, int64_t d,
+                              int32_t E, int32_t k, const moe_layout_t *layout, int32_t *counts,
+                              int32_t *expert_off, int32_t *chunk_off, int32_t *pair_slot,
+                              int32_t *row_pair, uint8_t *q_disp, float *q_scale, void *ws,
+                              size_t ws_bytes, void *stream);
+
 /* -------------------------------------------------------------- expert FFN
  * [EFA] MoE all-to-all over EFA: grouped GEMM kernels multiply the received tokens
  * with the expert weights; [EFA] Dispatch and combine: the receiver moves tokens
@@ -208,6 +225,14 @@ moe_status_t moe_ep_recv_plan(const int32_t *counts, const int32_t *chunk_off, i
                               int32_t *local_off, int32_t *row_src, void *stream);
 moe_status_t moe_ep_recv_gather(const void *x_region, const int32_t *row_src, int64_t cap,
                                 int64_t d, moe_dtype_t dtype, void *x_local, void *stream);
+/* moe_ep_recv_gather_fp8: x_local[j] = bf16(decode(q[row_src[j], i]) * scale[row_src[j], i/128])
+ * (the receiver's dequantization of the moe_dispatch_fp8 payload, one f32 product,
+ * one rounding); row_src NULL means row j itself (the expert-major layout). q_region
+ * [cap, d] uint8 (8-byte aligned), scale_region [cap, d/128] f32, x_local [cap, d]
+ * bf16; d % 128 == 0. */
+moe_status_t moe_ep_recv_gather_fp8(const uint8_t *q_region, const float *scale_region,
+                                    const int32_t *row_src, int64_t cap, int64_t d, void *x_local,
+                                    void *stream);
 moe_status_t moe_ep_recv_scatter(const void *y_local, const int32_t *row_src, int64_t cap,
                                  int64_t d, moe_dtype_t dtype, void *y_region, void *stream);
 

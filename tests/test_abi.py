@@ -120,3 +120,23 @@ def test_ep_recv_host_validation(lib):
     assert s(FAKE, None, 100, 64, BF16, FAKE, None) == INVALID
     assert s(None, None, 0, 64, BF16, None, None) == OK                         # nothing to do
     assert g(FAKE, FAKE, 1 << 31, 64, BF16, FAKE, None) == UNSUPPORTED
+
+
+def test_fp8_dispatch_host_validation(lib):
+    f = lib.moe_dispatch_fp8
+    ws_sz = lib.moe_dispatch_workspace_size(4096, 64, 6, None)
+    base = [FAKE, FAKE, 4096, 2048, 64, 6, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+            ws_sz, None]
+    bad = list(base); bad[3] = 2000                      # d % 128
+    assert f(*bad) == UNSUPPORTED
+    bad = list(base); bad[12] = None                     # no payload buffer
+    assert f(*bad) == INVALID
+    bad = list(base); bad[12] = FAKE + 8                 # codes not 16-byte aligned
+    assert f(*bad) == ALIGN
+    bad = list(base); bad[15] = ws_sz - 1
+    assert f(*bad) == CAPACITY
+    g = lib.moe_ep_recv_gather_fp8
+    assert g(FAKE, FAKE, None, 100, 2000, FAKE, None) == UNSUPPORTED
+    assert g(FAKE, FAKE + 4, None, 100, 2048, FAKE, None) == ALIGN
+    assert g(None, FAKE, None, 100, 2048, FAKE, None) == INVALID
+    assert g(None, None, None, 0, 2048, None, None) == OK

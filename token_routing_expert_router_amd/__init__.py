@@ -21,7 +21,8 @@ __all__ = ["MoEError", "load", "library_path", "moe_abi_version", "moe_route", "
            "moe_dispatch_status", "moe_expert_ffn", "moe_expert_ffn_gate_up",
            "moe_expert_ffn_down", "moe_combine", "moe_combine_bwd",
            "moe_expert_ffn_bwd", "moe_route_bwd", "moe_dispatch_bwd", "moe_ep_recv_plan",
-           "moe_ep_recv_gather", "moe_ep_recv_scatter", "Layout", "forward",
+           "moe_ep_recv_gather", "moe_ep_recv_scatter", "moe_dispatch_fp8",
+           "moe_ep_recv_gather_fp8", "Layout", "forward",
            "backward",
            "EXPORTED"]
 
@@ -58,6 +59,9 @@ EXPORTED = {
     "moe_route_bwd": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _P, _P, _P]),
     "moe_dispatch_bwd": (_I32, [_P, _P, _P, _P, _P, _I64, _I32, _I64, _I32, _I64, _I32, _P,
                                 _P]),
+    "moe_dispatch_fp8": (_I32, [_P, _P, _I64, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
+                                _P, _SZ, _P]),
+    "moe_ep_recv_gather_fp8": (_I32, [_P, _P, _P, _I64, _I64, _P, _P]),
     "moe_ep_recv_plan": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I64, _P, _P, _P]),
     "moe_ep_recv_gather": (_I32, [_P, _P, _I64, _I64, _I32, _P, _P]),
     "moe_ep_recv_scatter": (_I32, [_P, _P, _I64, _I64, _I32, _P, _P]),
@@ -185,6 +189,39 @@ def moe_dispatch(x, topk_idx, E: int, *, layout: Optional[Layout] = None, d: Opt
         _ptr(x), _ptr(topk_idx), T, d if d is not None else 8, E, k, dt, lay_ptr,
         _ptr(o["counts"]), _ptr(o["expert_off"]), _ptr(o["chunk_off"]), _ptr(o["pair_slot"]),
         _ptr(o["row_pair"]), _ptr(o["x_disp"]), _ptr(o["ws"]), o["ws"].numel(), _stream(stream)))
+    return o
+
+
+def moe_dispatch_fp8(x, topk_idx, E: int, *, layout: Optional[Layout] = None,
+                     out: Optional[dict] = None, stream=None):
+    """Plan + block-scaled fp8 payload (bf16 x, d % 128 == 0). Returns the plan dict
+    of moe_dispatch with q_disp (uint8 [rows, d]) and q_scale (float32 [rows, d/128])."""
+    T, k = topk_idx.shape
+    d = x.shape[1]
+    dev = x.device
+    n_src = layout.n_src if layout else 1
+    n_dst = layout.n_dst if layout else 1
+    cap = layout.cap if layout else T * k
+    lib = load()
+    clay = layout._c() if layout else None
+    lay_ptr = ctypes.byref(clay) if clay is not None else None
+    o = dict(out or {})
+    ws_bytes = int(lib.moe_dispatch_workspace_size(T, E, k, lay_ptr))
+    if o.get("ws") is None:
+        o["ws"] = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    for name, shape in (("counts", (n_src, E)), ("expert_off", (E + 1,)),
+                        ("chunk_off", (n_dst, n_src + 1)), ("pair_slot", (T, k)),
+                        ("row_pair", (n_dst * cap,))):
+        if o.get(name) is None:
+            o[name] = torch.empty(shape, dtype=torch.int32, device=dev)
+    if o.get("q_disp") is None:
+        o["q_disp"] = torch.empty((n_dst * cap, d), dtype=torch.uint8, device=dev)
+    if o.get("q_scale") is None:
+        o["q_scale"] = torch.empty((n_dst * cap, d // 128), dtype=torch.float32, device=dev)
+    _check("moe_dispatch_fp8", lib.moe_dispatch_fp8(
+        _ptr(x), _ptr(topk_idx), T, d, E, k, lay_ptr, _ptr(o["counts"]), _ptr(o["expert_off"]),
+        _ptr(o["chunk_off"]), _ptr(o["pair_slot"]), _ptr(o["row_pair"]), _ptr(o["q_disp"]),
+        _ptr(o["q_scale"]), _ptr(o["ws"]), o["ws"].numel(), _stream(stream)))
     return o
 
 
@@ -332,6 +369,17 @@ def moe_ep_recv_gather(x_region, row_src, *, x_local=None, stream=None):
         x_local = torch.empty_like(x_region)
     _check("moe_ep_recv_gather", load().moe_ep_recv_gather(
         _ptr(x_region), _ptr(row_src), cap, d, _dt(x_region), _ptr(x_local), _stream(stream)))
+    return x_local
+
+
+def moe_ep_recv_gather_fp8(q_region, scale_region, row_src=None, *, x_local=None, stream=None):
+    """x_local[j] = bf16(decode(q[row_src[j]]) * scale) (row j itself if row_src is None)."""
+    cap, d = q_region.shape
+    if x_local is None:
+        x_local = torch.empty((cap, d), dtype=torch.bfloat16, device=q_region.device)
+    _check("moe_ep_recv_gather_fp8", load().moe_ep_recv_gather_fp8(
+        _ptr(q_region), _ptr(scale_region), _ptr(row_src), cap, d, _ptr(x_local),
+        _stream(stream)))
     return x_local
 
 

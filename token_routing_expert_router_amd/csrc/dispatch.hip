@@ -243,10 +243,45 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_scan(
 constexpr int kSubTokens = 32;
 constexpr int kSubPerBlock = kPlanBlock / kSubTokens;
 
-__global__ __launch_bounds__(kPlanBlock) void k_plan_slots_copy(
+// Block-scaled fp8 payload of 16 consecutive elements (two 16-byte chunks of bf16) of
+// a row, for 8-lane groups that each hold one 128-element block: m = the block's
+// largest magnitude (an 8-lane max), scale = m / 448, codes = E4M3(x * (448 / m))
+// rounded to nearest even (the hardware conversion, its input clamped to +-448 so it
+// saturates); an all-zero block gets +0 codes.
+__device__ __forceinline__ uint4 quant16_fp8(const uint4 &v0, const uint4 &v1, float &scale) {
+    float f[16];
+    Vec<MOE_BF16>::unpack(v0, f);
+    Vec<MOE_BF16>::unpack(v1, f + 8);
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(f[i]));
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+    scale = m / 448.0f;
+    if (m == 0.0f) return make_uint4(0u, 0u, 0u, 0u);
+    const float inv = 448.0f / m;
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float r0 = fminf(fmaxf(f[4 * q] * inv, -448.0f), 448.0f);
+        const float r1 = fminf(fmaxf(f[4 * q + 1] * inv, -448.0f), 448.0f);
+        const float r2 = fminf(fmaxf(f[4 * q + 2] * inv, -448.0f), 448.0f);
+        const float r3 = fminf(fmaxf(f[4 * q + 3] * inv, -448.0f), 448.0f);
+        int p = __builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false);
+        p = __builtin_amdgcn_cvt_pk_fp8_f32(r2, r3, p, true);
+        w[q] = uint32_t(p);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+constexpr int kCopyThreads = 1024;   // 16 wavefronts share a sub-block's row copies
+
+template <bool Q8>
+__global__ __launch_bounds__(kCopyThreads) void k_plan_slots_copy(
     const int *__restrict__ idx, PlanGeom g, const int *__restrict__ blk_base,
     const int *__restrict__ chunk_off, int *__restrict__ pair_slot, int *__restrict__ row_pair,
-    int *__restrict__ flag, const uint4 *__restrict__ x, int rc, uint4 *__restrict__ x_disp) {
+    int *__restrict__ flag, const uint4 *__restrict__ x, int rc, uint4 *__restrict__ x_disp,
+    uint4 *__restrict__ q_disp, float *__restrict__ q_scale) {
     extern __shared__ unsigned long long masks[];
     __shared__ int sl[kSubTokens][32];
     const int b = blockIdx.x / kSubPerBlock, q = blockIdx.x % kSubPerBlock;
@@ -290,7 +325,25 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_slots_copy(
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int tcount = min(kSubTokens, n - q * kSubTokens);
-    for (int i = wave; i < tcount; i += kPlanBlock / kWave) {
+    if (Q8) {
+        // a row is rc/2 pieces of 16 elements (16 code bytes); 8 lanes hold one block
+        const int rp = rc / 2, nb = rc / 16;
+        for (int i = wave; i < tcount; i += kCopyThreads / kWave) {
+            const uint4 *src = x + size_t(t_begin + q * kSubTokens + i) * rc;
+            for (int c = lane; c < rp; c += kWave) {
+                float sc;
+                const uint4 code = quant16_fp8(src[2 * c], src[2 * c + 1], sc);
+                for (int j = 0; j < g.k; ++j) {
+                    const int sj = sl[i][j];
+                    if (sj < 0 || sj >= rows_total) continue;
+                    q_disp[size_t(sj) * rp + c] = code;
+                    if ((lane & 7) == 0) q_scale[size_t(sj) * nb + c / 8] = sc;
+                }
+            }
+        }
+        return;
+    }
+    for (int i = wave; i < tcount; i += kCopyThreads / kWave) {
         const uint4 *src = x + size_t(t_begin + q * kSubTokens + i) * rc;
         int c = lane;
         for (; c + 3 * kWave < rc; c += 4 * kWave) {
@@ -383,12 +436,16 @@ extern "C" size_t moe_dispatch_workspace_size(int64_t T, int32_t E, int32_t k,
     return ws_bytes_for(make_geom(T, E, k, layout));
 }
 
-extern "C" moe_status_t moe_dispatch(const void *x, const int32_t *topk_idx, int64_t T,
-                                     int64_t d, int32_t E, int32_t k, moe_dtype_t dtype,
-                                     const moe_layout_t *layout, int32_t *counts,
-                                     int32_t *expert_off, int32_t *chunk_off, int32_t *pair_slot,
-                                     int32_t *row_pair, void *x_disp, void *ws, size_t ws_bytes,
-                                     void *stream) {
+namespace moe {
+namespace {
+
+// The plan, then either the row copy (x_disp) or the fp8 payload (q_disp, q_scale).
+moe_status_t dispatch_impl(const void *x, const int32_t *topk_idx, int64_t T, int64_t d,
+                           int32_t E, int32_t k, moe_dtype_t dtype, const moe_layout_t *layout,
+                           int32_t *counts, int32_t *expert_off, int32_t *chunk_off,
+                           int32_t *pair_slot, int32_t *row_pair, void *x_disp, uint8_t *q_disp,
+                           float *q_scale, void *ws, size_t ws_bytes, void *stream) {
+    const bool q8 = q_disp != nullptr || q_scale != nullptr;
     if (!valid_dtype(dtype) || T < 0 || d <= 0 || E <= 0 || k <= 0) return MOE_ERR_INVALID_ARG;
     if (k > E) return MOE_ERR_SHAPE;
     if (layout && (layout->n_src <= 0 || layout->n_dst <= 0 || layout->cap_rows_per_dst < 0))
@@ -409,11 +466,15 @@ extern "C" moe_status_t moe_dispatch(const void *x, const int32_t *topk_idx, int
     if (T == 0) return MOE_OK;
     if (!topk_idx || !counts || !expert_off || !chunk_off || !pair_slot || !row_pair || !ws)
         return MOE_ERR_INVALID_ARG;
-    if ((x == nullptr) != (x_disp == nullptr)) return MOE_ERR_INVALID_ARG;
+    if (!q8 && (x == nullptr) != (x_disp == nullptr)) return MOE_ERR_INVALID_ARG;
+    if (q8 && (!x || !q_disp || !q_scale)) return MOE_ERR_INVALID_ARG;
+    if (q8 && (dtype != MOE_BF16 || d % 128 != 0)) return MOE_ERR_UNSUPPORTED;
     if (ws_bytes < ws_bytes_for(g)) return MOE_ERR_CAPACITY;
     if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return MOE_ERR_ALIGN;
     const int64_t rowb = d * elt_size(dtype);
-    if (x && (rowb % 16 != 0 || !aligned16(x) || !aligned16(x_disp))) return MOE_ERR_ALIGN;
+    if (x && (rowb % 16 != 0 || !aligned16(x) || (!q8 && !aligned16(x_disp)))) return MOE_ERR_ALIGN;
+    if (q8 && (!aligned16(q_disp) || !aligned16(q_scale)))
+        return MOE_ERR_ALIGN;
 
     if (!set_scan_lds_limit()) return MOE_ERR_HIP;   // first HIP call: all checks done
     const hipStream_t st = as_stream(stream);
@@ -428,10 +489,41 @@ extern "C" moe_status_t moe_dispatch(const void *x, const int32_t *topk_idx, int
                        blk_counts, blk_flags);
     hipLaunchKernelGGL(k_plan_scan, dim3(1), dim3(kScanThreads), lds_scan, st, blk_counts,
                        blk_flags, g, counts, expert_off, chunk_off, blk_base, flag);
-    hipLaunchKernelGGL(k_plan_slots_copy, dim3(g.B * kSubPerBlock), dim3(kPlanBlock), lds_mask, st,
-                       topk_idx, g, blk_base, chunk_off, pair_slot, row_pair, flag,
-                       static_cast<const uint4 *>(x), int(rowb / 16), static_cast<uint4 *>(x_disp));
+    if (q8)
+        hipLaunchKernelGGL(k_plan_slots_copy<true>, dim3(g.B * kSubPerBlock), dim3(kCopyThreads),
+                           lds_mask, st, topk_idx, g, blk_base, chunk_off, pair_slot, row_pair, flag,
+                           static_cast<const uint4 *>(x), int(rowb / 16), nullptr,
+                           reinterpret_cast<uint4 *>(q_disp), q_scale);
+    else
+        hipLaunchKernelGGL(k_plan_slots_copy<false>, dim3(g.B * kSubPerBlock), dim3(kCopyThreads),
+                           lds_mask, st, topk_idx, g, blk_base, chunk_off, pair_slot, row_pair, flag,
+                           static_cast<const uint4 *>(x), int(rowb / 16), static_cast<uint4 *>(x_disp),
+                           nullptr, nullptr);
     return launch_status();
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" moe_status_t moe_dispatch(const void *x, const int32_t *topk_idx, int64_t T,
+                                     int64_t d, int32_t E, int32_t k, moe_dtype_t dtype,
+                                     const moe_layout_t *layout, int32_t *counts,
+                                     int32_t *expert_off, int32_t *chunk_off, int32_t *pair_slot,
+                                     int32_t *row_pair, void *x_disp, void *ws, size_t ws_bytes,
+                                     void *stream) {
+    return dispatch_impl(x, topk_idx, T, d, E, k, dtype, layout, counts, expert_off, chunk_off,
+                         pair_slot, row_pair, x_disp, nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+extern "C" moe_status_t moe_dispatch_fp8(const void *x, const int32_t *topk_idx, int64_t T,
+                                         int64_t d, int32_t E, int32_t k,
+                                         const moe_layout_t *layout, int32_t *counts,
+                                         int32_t *expert_off, int32_t *chunk_off,
+                                         int32_t *pair_slot, int32_t *row_pair, uint8_t *q_disp,
+                                         float *q_scale, void *ws, size_t ws_bytes, void *stream) {
+    if (!q_disp || !q_scale) return MOE_ERR_INVALID_ARG;
+    return dispatch_impl(x, topk_idx, T, d, E, k, MOE_BF16, layout, counts, expert_off, chunk_off,
+                         pair_slot, row_pair, nullptr, q_disp, q_scale, ws, ws_bytes, stream);
 }
 
 extern "C" moe_status_t moe_dispatch_status(const void *ws, void *stream) {

@@ -84,6 +84,40 @@ __global__ __launch_bounds__(256) void k_ep_rows(const uint4 *__restrict__ src,
     }
 }
 
+// Gather with dequantization of the block-scaled fp8 payload: x_local[j] =
+// bf16(decode(code) * scale) of region row row_src[j] (row j itself when row_src is
+// null). A lane holds 8 codes (8 bytes) of a row; 16 lanes share one 128-element block.
+__global__ __launch_bounds__(256) void k_ep_rows_fp8(const uint2 *__restrict__ q,
+                                                     const float *__restrict__ qs,
+                                                     const int *__restrict__ row_src, int cap,
+                                                     int rc, uint4 *__restrict__ dst) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wpb = blockDim.x / kWave;
+    const int w0 = blockIdx.x * wpb + threadIdx.x / kWave;
+    const int nb = rc / 16;
+    for (int j = w0; j < cap; j += gridDim.x * wpb) {
+        const int src = row_src ? row_src[j] : j;
+        if (src < 0 || src >= cap) continue;
+        const uint2 *qr = q + size_t(src) * rc;
+        const float *sr = qs + size_t(src) * nb;
+        uint4 *o = dst + size_t(j) * rc;
+        for (int c = lane; c < rc; c += kWave) {
+            const uint2 w = qr[c];
+            const float sc = sr[c / 16];
+            float f[8];
+            f[0] = __builtin_amdgcn_cvt_f32_fp8(int(w.x), 0) * sc;
+            f[1] = __builtin_amdgcn_cvt_f32_fp8(int(w.x), 1) * sc;
+            f[2] = __builtin_amdgcn_cvt_f32_fp8(int(w.x), 2) * sc;
+            f[3] = __builtin_amdgcn_cvt_f32_fp8(int(w.x), 3) * sc;
+            f[4] = __builtin_amdgcn_cvt_f32_fp8(int(w.y), 0) * sc;
+            f[5] = __builtin_amdgcn_cvt_f32_fp8(int(w.y), 1) * sc;
+            f[6] = __builtin_amdgcn_cvt_f32_fp8(int(w.y), 2) * sc;
+            f[7] = __builtin_amdgcn_cvt_f32_fp8(int(w.y), 3) * sc;
+            o[c] = Vec<MOE_BF16>::pack(f);
+        }
+    }
+}
+
 moe_status_t check_rows(const void *a, const void *row_src, int64_t cap, int64_t d,
                         moe_dtype_t dtype, const void *b) {
     if (!valid_dtype(dtype) || cap < 0 || d <= 0) return MOE_ERR_INVALID_ARG;
@@ -132,6 +166,25 @@ extern "C" moe_status_t moe_ep_recv_gather(const void *x_region, const int32_t *
                                            int64_t cap, int64_t d, moe_dtype_t dtype,
                                            void *x_local, void *stream) {
     return launch_rows<true>(x_region, row_src, cap, d, dtype, x_local, stream);
+}
+
+extern "C" moe_status_t moe_ep_recv_gather_fp8(const uint8_t *q_region, const float *scale_region,
+                                               const int32_t *row_src, int64_t cap, int64_t d,
+                                               void *x_local, void *stream) {
+    if (cap < 0 || d <= 0) return MOE_ERR_INVALID_ARG;
+    if (cap >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+    if (cap == 0) return MOE_OK;
+    if (!q_region || !scale_region || !x_local) return MOE_ERR_INVALID_ARG;
+    if (d % 128 != 0) return MOE_ERR_UNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(q_region) & 7u) != 0 || !aligned16(scale_region) ||
+        !aligned16(x_local))
+        return MOE_ERR_ALIGN;
+    const int rc = int(d / 8);
+    const int g = int(std::min<int64_t>(cdiv(cap, 4), 2048));
+    hipLaunchKernelGGL(k_ep_rows_fp8, dim3(g), dim3(256), 0, as_stream(stream),
+                       reinterpret_cast<const uint2 *>(q_region), scale_region, row_src, int(cap),
+                       rc, static_cast<uint4 *>(x_local));
+    return launch_status();
 }
 
 extern "C" moe_status_t moe_ep_recv_scatter(const void *y_local, const int32_t *row_src,
