@@ -36,6 +36,8 @@ trillion-parameter models on AWS EFA" (N. Licker, K. Hu, V. Zaytsev, L. Chen,
                   local expert's rows are contiguous before its grouped GEMM ([EFA]
                   Dispatch and combine, receiver side); senders ascending inside an
                   expert (a stable reading: the pages leave the order open).
+* partial combine destinations sum each token's gate-weighted outputs before the
+                  return; one row per (token, destination) travels back.
 * backward        the transposes of the above, and the softmax-over-top-k Jacobian.
 
 Precision: everything is float64 except the router logits, which decide integers and
@@ -310,6 +312,45 @@ def ep_recv_plan(counts, chunk_off, r: int, n_dst: int, cap: int):
     out = np.full(cap, -1, dtype=np.int64)
     out[:len(row_src)] = row_src
     return local_off, out
+
+
+# ------------------------------------------------- partial combine (rank-major layout)
+def combine_partial(y_disp, pair_slot, gates, n_dst: int, cap: int, round_to=None):
+    """Partial sums at the destinations: for token t and destination r holding rows of t
+    (rows [r*cap, (r+1)*cap)), partial[r, t] = sum over those j of g[t,j] y_disp[slot],
+    float64 in j order, then rounded by round_to (the return payload's precision; None
+    keeps float64). The article accumulates at the combine's receiver only ([EFA]
+    Dispatch/combine latency); summing at the destinations first is the variant that
+    sends one row per (token, destination). Returns (partial [n_dst, T, d], present
+    [n_dst, T] bool)."""
+    y_disp = _f64(y_disp)
+    pair_slot = np.asarray(pair_slot, dtype=np.int64)
+    gates = np.asarray(gates, dtype=np.float64)
+    T, k = pair_slot.shape
+    d = y_disp.shape[1]
+    partial = np.zeros((n_dst, T, d), dtype=np.float64)
+    present = np.zeros((n_dst, T), dtype=bool)
+    for t in range(T):
+        for j in range(k):
+            s = int(pair_slot[t, j])
+            if s < 0 or s >= n_dst * cap:
+                continue
+            r = s // cap
+            partial[r, t] += gates[t, j] * y_disp[s]
+            present[r, t] = True
+    if round_to is not None:
+        partial = round_to(partial)
+    return partial, present
+
+
+def combine_from_partials(partial, present) -> np.ndarray:
+    """y[t] = sum over the destinations r with rows of t, r ascending, of partial[r, t]."""
+    partial = np.asarray(partial, dtype=np.float64)
+    n_dst, T, d = partial.shape
+    y = np.zeros((T, d), dtype=np.float64)
+    for r in range(n_dst):
+        y += np.where(np.asarray(present)[r][:, None], partial[r], 0.0)
+    return y
 
 
 # ----------------------------------------------------------------------- dispatch

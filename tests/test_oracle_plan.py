@@ -179,3 +179,60 @@ def test_ep_recv_plan_matches_expert_major_layout():
         assert np.array_equal(off, p_em["expert_off"][r * epr:(r + 1) * epr + 1] - lo)
         pairs_local = p_ep["row_pair"][r * cap + src[:live]]
         assert np.array_equal(pairs_local, em_pair_of_row[lo:hi])
+
+
+# ------------------------------------------------------------ partial combine
+def _bf16_round(a):
+    import torch
+    return torch.from_numpy(np.asarray(a, dtype=np.float32)).to(torch.bfloat16).double().numpy()
+
+
+def test_combine_partial_golden():
+    """The 2-sender, 2-destination example with y_disp row i = (i + 1) * ones(2) and
+    gates 0.5 / 0.25 / ...: worked by hand from its pair_slot."""
+    case = json.load(open(os.path.join(GOLDEN, "plan_examples.json")))["cases"][1]
+    ps = np.array(case["pair_slot"])
+    y_disp = np.repeat(np.arange(1, 25, dtype=np.float64)[:, None], 2, axis=1)
+    g = np.tile([0.75, 0.25], (6, 1))
+    partial, present = oracle.combine_partial(y_disp, ps, g, 2, case["cap"])
+    # token 0: slots (2, 12) -> r=0 gets 0.75*3, r=1 gets 0.25*13
+    assert partial[0, 0, 0] == 0.75 * 3 and partial[1, 0, 0] == 0.25 * 13
+    # token 1: slots (0, 3) both at r=0: 0.75*1 + 0.25*4
+    assert partial[0, 1, 0] == 0.75 * 1 + 0.25 * 4 and not present[1, 1]
+    assert present.sum() == 10     # tokens 0, 2, 4, 5 split (2 each); 1 at r=0; 3 at r=1
+
+
+@pytest.mark.parametrize("n_src,n_dst", [(1, 1), (4, 2), (2, 8)])
+def test_combine_partial_unrounded_equals_combine(n_src, n_dst):
+    """Without the payload rounding, summing partials is combine() reordered."""
+    rng = np.random.default_rng(n_dst)
+    T, E, k, d = 64, 16, 4, 8
+    idx = _random_idx(rng, T, E, k)
+    cap = n_src * (T // n_src) * max(k, E // n_dst)
+    p = oracle.plan(idx, E, n_src, n_dst, cap)
+    y_disp = rng.normal(size=(n_dst * cap, d))
+    g = rng.uniform(0.1, 1, (T, k))
+    partial, present = oracle.combine_partial(y_disp, p["pair_slot"], g, n_dst, cap)
+    got = oracle.combine_from_partials(partial, present)
+    ref = oracle.combine(y_disp, p["pair_slot"], g)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+    dests = p["pair_slot"] // cap
+    for t in range(T):
+        assert set(np.nonzero(present[:, t])[0]) == set(dests[t].tolist())
+
+
+def test_combine_partial_rounding_bound():
+    """With bf16 payloads the sum moves by at most half an ulp per partial."""
+    rng = np.random.default_rng(5)
+    T, E, k, d, n_src, n_dst = 32, 8, 3, 16, 2, 4
+    idx = _random_idx(rng, T, E, k)
+    cap = n_src * (T // n_src) * max(k, E // n_dst)
+    p = oracle.plan(idx, E, n_src, n_dst, cap)
+    y_disp = rng.normal(size=(n_dst * cap, d))
+    g = rng.uniform(0.1, 1, (T, k))
+    exact, present = oracle.combine_partial(y_disp, p["pair_slot"], g, n_dst, cap)
+    rounded, _ = oracle.combine_partial(y_disp, p["pair_slot"], g, n_dst, cap, _bf16_round)
+    diff = np.abs(oracle.combine_from_partials(rounded, present)
+                  - oracle.combine_from_partials(exact, present))
+    bound = (np.abs(exact) * 2.0 ** -8).sum(axis=0)
+    assert np.all(diff <= bound + 1e-300)
