@@ -250,9 +250,36 @@ def ep_bench(torch, moe, wl, dev, steps, warmup):
            "max_rows_per_dst": int(live.max()), "stages": stages}
     out["receive_rank0"] = ep_receive_bench(torch, moe, wl, plan, steps, warmup)
     out["fp8"] = ep_fp8_bench(torch, moe, wl, x, idx, plan, lay, steps, warmup)
+    out["partial_combine"] = ep_partial_bench(torch, moe, wl, plan, w, steps, warmup)
     del plan, x
     torch.cuda.empty_cache()
     return out
+
+
+def ep_partial_bench(torch, moe, wl, plan, w, steps, warmup):
+    """Combine with the destinations' partial sums: one row per (token, destination)
+    returns instead of one per (token, expert) (identity experts)."""
+    cap, d, T = wl.cap_rows_per_dst, wl.d, wl.T
+    part = moe.moe_combine_partial(plan["x_disp"], plan["pair_slot"], w, wl.n_dst, cap)
+    y = torch.empty((T, d), dtype=torch.bfloat16, device=part.device)
+
+    def step(ev):
+        ev[0].record()
+        moe.moe_combine_partial(plan["x_disp"], plan["pair_slot"], w, wl.n_dst, cap, partial=part)
+        ev[1].record()
+        moe.moe_combine_partials(part, plan["pair_slot"], wl.n_dst, cap, y=y)
+        ev[2].record()
+
+    elapsed, events = timed(torch, step, 2, steps, warmup)
+    dests = (plan["pair_slot"] // cap).sort(dim=1).values
+    n_ret = int(T + (dests[:, 1:] != dests[:, :-1]).sum())
+    P, b = T * wl.k, 2
+    work = {"combine_partial": dict(bytes=P * d * b + n_ret * d * b + P * 8, flops=0, unit="hbm"),
+            "combine_partials": dict(bytes=n_ret * d * b + T * d * b, flops=0, unit="hbm")}
+    stages = summarize(["combine_partial", "combine_partials"], events, steps, work)
+    res = {"return_rows": n_ret, "per_expert_rows": P, "stages": stages}
+    del part, y
+    return res
 
 
 def ep_fp8_bench(torch, moe, wl, x, idx, plan, lay, steps, warmup, r=0):

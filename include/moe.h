@@ -236,6 +236,28 @@ moe_status_t moe_ep_recv_gather_fp8(const uint8_t *q_region, const float *scale_
 moe_status_t moe_ep_recv_scatter(const void *y_local, const int32_t *row_src, int64_t cap,
                                  int64_t d, moe_dtype_t dtype, void *y_region, void *stream);
 
+/* ------------------------------------------------ partial combine (rank-major)
+ * [EFA] Dispatch/combine latency: the article accumulates only at the receiver of the
+ * combine. The variant here lets each destination of the rank-major layout first sum,
+ * per token, the gate-weighted outputs of that token's experts it holds, so one row per
+ * (token, destination) travels back instead of one per (token, expert); the source
+ * then adds its partial rows. The partial is rounded to dtype before the return (the
+ * payload precision), so the result carries one more rounding than moe_combine.
+ *   moe_combine_partial:  partial[r*T + t] = sum_{j: pair_slot[t,j] in [r*cap,(r+1)*cap)}
+ *                         topk_w[t,j] * y_disp[pair_slot[t,j]]      (float32 fma in j
+ *                         order, one rounding); rows of absent (t, r) are not written
+ *   moe_combine_partials: y[t] = sum over the destinations r holding rows of t, r
+ *                         ascending, of partial[r*T + t]   (float32, one rounding)
+ * partial [n_dst*T, d] dtype; other arguments as for moe_combine with rows_total =
+ * n_dst*cap; n_dst <= 64 and k <= 64, else MOE_ERR_UNSUPPORTED. */
+moe_status_t moe_combine_partial(const void *y_disp, const int32_t *pair_slot,
+                                 const float *topk_w, int64_t T, int32_t k, int64_t d,
+                                 int32_t n_dst, int64_t cap, moe_dtype_t dtype, void *partial,
+                                 void *stream);
+moe_status_t moe_combine_partials(const void *partial, const int32_t *pair_slot, int64_t T,
+                                  int32_t k, int64_t d, int32_t n_dst, int64_t cap,
+                                  moe_dtype_t dtype, void *y, void *stream);
+
 /* ---------------------------------------------------------------- backward
  * The transposes of the steps above (the layer's gradient; the article covers
  * only the forward data movement).

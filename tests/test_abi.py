@@ -140,3 +140,12 @@ def test_fp8_dispatch_host_validation(lib):
     assert g(FAKE, FAKE + 4, None, 100, 2048, FAKE, None) == ALIGN
     assert g(None, FAKE, None, 100, 2048, FAKE, None) == INVALID
     assert g(None, None, None, 0, 2048, None, None) == OK
+
+
+def test_partial_combine_host_validation(lib):
+    p, q = lib.moe_combine_partial, lib.moe_combine_partials
+    assert p(FAKE, FAKE, FAKE, 10, 2, 64, 65, 100, BF16, FAKE, None) == UNSUPPORTED   # n_dst
+    assert p(FAKE, FAKE, None, 10, 2, 64, 4, 100, BF16, FAKE, None) == INVALID        # gates
+    assert p(FAKE, FAKE, FAKE, 10, 2, 60, 4, 100, BF16, FAKE, None) == ALIGN
+    assert q(FAKE, FAKE, 10, 2, 64, 0, 100, BF16, FAKE, None) == INVALID              # n_dst 0
+    assert q(None, None, 0, 2, 64, 4, 100, BF16, None, None) == OK

@@ -22,7 +22,7 @@ __all__ = ["MoEError", "load", "library_path", "moe_abi_version", "moe_route", "
            "moe_expert_ffn_down", "moe_combine", "moe_combine_bwd",
            "moe_expert_ffn_bwd", "moe_route_bwd", "moe_dispatch_bwd", "moe_ep_recv_plan",
            "moe_ep_recv_gather", "moe_ep_recv_scatter", "moe_dispatch_fp8",
-           "moe_ep_recv_gather_fp8", "Layout", "forward",
+           "moe_ep_recv_gather_fp8", "moe_combine_partial", "moe_combine_partials", "Layout", "forward",
            "backward",
            "EXPORTED"]
 
@@ -62,6 +62,8 @@ EXPORTED = {
     "moe_dispatch_fp8": (_I32, [_P, _P, _I64, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
                                 _P, _SZ, _P]),
     "moe_ep_recv_gather_fp8": (_I32, [_P, _P, _P, _I64, _I64, _P, _P]),
+    "moe_combine_partial": (_I32, [_P, _P, _P, _I64, _I32, _I64, _I32, _I64, _I32, _P, _P]),
+    "moe_combine_partials": (_I32, [_P, _P, _I64, _I32, _I64, _I32, _I64, _I32, _P, _P]),
     "moe_ep_recv_plan": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I64, _P, _P, _P]),
     "moe_ep_recv_gather": (_I32, [_P, _P, _I64, _I64, _I32, _P, _P]),
     "moe_ep_recv_scatter": (_I32, [_P, _P, _I64, _I64, _I32, _P, _P]),
@@ -342,6 +344,31 @@ def moe_dispatch_bwd(dx_disp, pair_slot, *, topk_idx=None, dlogits_sel=None, w_r
         _ptr(dx_disp), _ptr(pair_slot), _ptr(topk_idx), _ptr(dlogits_sel), _ptr(w_router), T, k,
         d, E, rows, _dt(dx_disp), _ptr(dx), _stream(stream)))
     return dx
+
+
+def moe_combine_partial(y_disp, pair_slot, topk_w, n_dst: int, cap: int, *, partial=None,
+                        stream=None):
+    """Per (token, destination) gate-weighted partial sums [n_dst*T, d] (rank-major)."""
+    T, k = pair_slot.shape
+    d = y_disp.shape[1]
+    if partial is None:
+        partial = torch.empty((n_dst * T, d), dtype=y_disp.dtype, device=y_disp.device)
+    _check("moe_combine_partial", load().moe_combine_partial(
+        _ptr(y_disp), _ptr(pair_slot), _ptr(topk_w), T, k, d, n_dst, cap, _dt(y_disp),
+        _ptr(partial), _stream(stream)))
+    return partial
+
+
+def moe_combine_partials(partial, pair_slot, n_dst: int, cap: int, *, y=None, stream=None):
+    """y[t] = sum over t's destinations (ascending) of partial[r*T + t]."""
+    T, k = pair_slot.shape
+    d = partial.shape[1]
+    if y is None:
+        y = torch.empty((T, d), dtype=partial.dtype, device=partial.device)
+    _check("moe_combine_partials", load().moe_combine_partials(
+        _ptr(partial), _ptr(pair_slot), T, k, d, n_dst, cap, _dt(partial), _ptr(y),
+        _stream(stream)))
+    return y
 
 
 # ------------------------------------------------- receive side (rank-major layout)

@@ -86,6 +86,95 @@ __global__ __launch_bounds__(256) void k_combine_bwd(const uint4 *__restrict__ d
     }
 }
 
+// Partial combine at the destinations of the rank-major layout: for every token t and
+// every destination r holding rows of t (rows [r*cap, (r+1)*cap)), the gate-weighted
+// sum of t's rows at r, float32 fused multiply-adds in j order, one rounding:
+// partial[r*T + t] (rows of tokens without rows at r are not written). Lane j < k of
+// the token's wavefront holds slot j and its destination; the wavefront's set of
+// destinations is a 64-bit mask (n_dst <= 64).
+__device__ __forceinline__ uint64_t wave_or64(uint64_t v) {
+    uint32_t lo = uint32_t(v), hi = uint32_t(v >> 32);
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        lo |= __shfl_xor(lo, off, kWave);
+        hi |= __shfl_xor(hi, off, kWave);
+    }
+    return (uint64_t(hi) << 32) | lo;
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_combine_partial(const uint4 *__restrict__ y_disp,
+                                                         const int *__restrict__ pair_slot,
+                                                         const float *__restrict__ topk_w, int T,
+                                                         int k, int rc, int n_dst, int cap,
+                                                         uint4 *__restrict__ partial) {
+    constexpr int VN = Vec<DT>::N;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave0 = __builtin_amdgcn_readfirstlane((blockIdx.x * blockDim.x + threadIdx.x) / kWave);
+    const int nwaves = gridDim.x * blockDim.x / kWave;
+    const int rows_total = n_dst * cap;
+    for (int t = wave0; t < T; t += nwaves) {
+        const int my_s = lane < k ? pair_slot[size_t(t) * k + lane] : -1;
+        const bool ok = my_s >= 0 && my_s < rows_total;
+        const int my_r = ok ? my_s / cap : -1;
+        const float my_g = lane < k ? topk_w[size_t(t) * k + lane] : 0.0f;
+        uint64_t dm = wave_or64(ok ? (uint64_t(1) << my_r) : 0);
+        while (dm) {
+            const int r = __builtin_ctzll(dm);
+            dm &= dm - 1;
+            for (int c = lane; c < rc; c += kWave) {
+                float acc[VN];
+#pragma unroll
+                for (int i = 0; i < VN; ++i) acc[i] = 0.0f;
+                for (int j = 0; j < k; ++j) {
+                    if (__shfl(my_r, j, kWave) != r) continue;
+                    const int s = __shfl(my_s, j, kWave);
+                    const float g = __shfl(my_g, j, kWave);
+                    float f[VN];
+                    Vec<DT>::unpack(y_disp[size_t(s) * rc + c], f);
+#pragma unroll
+                    for (int i = 0; i < VN; ++i) acc[i] = __builtin_fmaf(g, f[i], acc[i]);
+                }
+                partial[(size_t(r) * T + t) * rc + c] = Vec<DT>::pack(acc);
+            }
+        }
+    }
+}
+
+// The sources' side: y[t] = sum over the destinations r holding rows of t, in ascending
+// r, of partial[r*T + t] (float32 additions, one rounding).
+template <int DT>
+__global__ __launch_bounds__(256) void k_combine_partials(const uint4 *__restrict__ partial,
+                                                          const int *__restrict__ pair_slot,
+                                                          int T, int k, int rc, int n_dst,
+                                                          int cap, uint4 *__restrict__ y) {
+    constexpr int VN = Vec<DT>::N;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave0 = __builtin_amdgcn_readfirstlane((blockIdx.x * blockDim.x + threadIdx.x) / kWave);
+    const int nwaves = gridDim.x * blockDim.x / kWave;
+    const int rows_total = n_dst * cap;
+    for (int t = wave0; t < T; t += nwaves) {
+        const int my_s = lane < k ? pair_slot[size_t(t) * k + lane] : -1;
+        const bool ok = my_s >= 0 && my_s < rows_total;
+        const uint64_t dm0 = wave_or64(ok ? (uint64_t(1) << (my_s / cap)) : 0);
+        for (int c = lane; c < rc; c += kWave) {
+            float acc[VN];
+#pragma unroll
+            for (int i = 0; i < VN; ++i) acc[i] = 0.0f;
+            uint64_t dm = dm0;
+            while (dm) {
+                const int r = __builtin_ctzll(dm);
+                dm &= dm - 1;
+                float f[VN];
+                Vec<DT>::unpack(partial[(size_t(r) * T + t) * rc + c], f);
+#pragma unroll
+                for (int i = 0; i < VN; ++i) acc[i] += f[i];
+            }
+            y[size_t(t) * rc + c] = Vec<DT>::pack(acc);
+        }
+    }
+}
+
 int row_grid(int64_t T) { return int(std::min<int64_t>(cdiv(T, 4), 8192)); }
 
 }  // namespace
@@ -139,5 +228,58 @@ extern "C" moe_status_t moe_combine_bwd(const void *dy, const void *y_disp,
                            static_cast<const uint4 *>(dy), static_cast<const uint4 *>(y_disp),
                            pair_slot, topk_w, int(T), k, int(rowb / 16), rows_total,
                            static_cast<uint4 *>(dy_disp), dtopk_w);
+    return launch_status();
+}
+
+namespace {
+moe_status_t check_partial(const void *a, const int32_t *pair_slot, int64_t T, int32_t k,
+                           int64_t d, int32_t n_dst, int64_t cap, moe_dtype_t dtype, const void *b) {
+    if (!valid_dtype(dtype) || T < 0 || d <= 0 || k <= 0 || n_dst <= 0 || cap <= 0)
+        return MOE_ERR_INVALID_ARG;
+    if (n_dst > 64 || k > 64 || int64_t(n_dst) * cap >= (int64_t(1) << 31) ||
+        int64_t(n_dst) * T >= (int64_t(1) << 31))
+        return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!a || !pair_slot || !b) return MOE_ERR_INVALID_ARG;
+    if ((d * elt_size(dtype)) % 16 != 0 || !aligned16(a) || !aligned16(b)) return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+}  // namespace
+
+extern "C" moe_status_t moe_combine_partial(const void *y_disp, const int32_t *pair_slot,
+                                            const float *topk_w, int64_t T, int32_t k, int64_t d,
+                                            int32_t n_dst, int64_t cap, moe_dtype_t dtype,
+                                            void *partial, void *stream) {
+    const moe_status_t c = check_partial(y_disp, pair_slot, T, k, d, n_dst, cap, dtype, partial);
+    if (c != MOE_OK || T == 0) return c;
+    if (!topk_w) return MOE_ERR_INVALID_ARG;
+    const int rc = int(d * elt_size(dtype) / 16);
+    const hipStream_t st = as_stream(stream);
+    if (dtype == MOE_BF16)
+        hipLaunchKernelGGL(k_combine_partial<MOE_BF16>, dim3(row_grid(T)), dim3(256), 0, st,
+                           static_cast<const uint4 *>(y_disp), pair_slot, topk_w, int(T), k, rc,
+                           n_dst, int(cap), static_cast<uint4 *>(partial));
+    else
+        hipLaunchKernelGGL(k_combine_partial<MOE_F32>, dim3(row_grid(T)), dim3(256), 0, st,
+                           static_cast<const uint4 *>(y_disp), pair_slot, topk_w, int(T), k, rc,
+                           n_dst, int(cap), static_cast<uint4 *>(partial));
+    return launch_status();
+}
+
+extern "C" moe_status_t moe_combine_partials(const void *partial, const int32_t *pair_slot,
+                                             int64_t T, int32_t k, int64_t d, int32_t n_dst,
+                                             int64_t cap, moe_dtype_t dtype, void *y, void *stream) {
+    const moe_status_t c = check_partial(partial, pair_slot, T, k, d, n_dst, cap, dtype, y);
+    if (c != MOE_OK || T == 0) return c;
+    const int rc = int(d * elt_size(dtype) / 16);
+    const hipStream_t st = as_stream(stream);
+    if (dtype == MOE_BF16)
+        hipLaunchKernelGGL(k_combine_partials<MOE_BF16>, dim3(row_grid(T)), dim3(256), 0, st,
+                           static_cast<const uint4 *>(partial), pair_slot, int(T), k, rc, n_dst,
+                           int(cap), static_cast<uint4 *>(y));
+    else
+        hipLaunchKernelGGL(k_combine_partials<MOE_F32>, dim3(row_grid(T)), dim3(256), 0, st,
+                           static_cast<const uint4 *>(partial), pair_slot, int(T), k, rc, n_dst,
+                           int(cap), static_cast<uint4 *>(y));
     return launch_status();
 }
