@@ -11,6 +11,8 @@ E=64, k=6, F=1408 bf16 layer. The same JSON line also reports:
                tokens, d=7168, E=384, k=8, Zipf(1.2) routing (identity experts), and
                destination 0's receive path (reorder, 12-expert SwiGLU GEMM, scatter),
   large        the T=8192, d=7168, E=384, k=8, F=2048 layer forward (34 GB weights),
+  overlap      the headline layer with a shared expert on a second stream, and with two
+               micro-batches on two streams, each against its one-stream form,
   roofline     the dominant kernel of the headline step, timed live with HIP events,
   cpu_baseline the CPU oracle on the host cores over whole passes of the headline
                workload.
@@ -47,6 +49,8 @@ def parse():
     ap.add_argument("--no-large", action="store_true", help="skip the 34 GB large-layer run")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--only-overlap", action="store_true",
+                    help="run only the two-stream shared-expert and micro-batch forms")
     ap.add_argument("--only-ep", action="store_true",
                     help="run only the rank-major dispatch/combine and receive path")
     ap.add_argument("--only-train", action="store_true",
@@ -360,6 +364,46 @@ def ep_receive_bench(torch, moe, wl, plan, steps, warmup, r=0, F=2048):
     return res
 
 
+def overlap_bench(torch, moe, wl, dev, steps, warmup):
+    """Two-stream forms of the headline layer: (a) plus a shared expert (SwiGLU, F as the
+    routed experts) run on a second stream during the routed path, against the same
+    calls on one stream; (b) two micro-batches on two streams against the whole batch."""
+    import moe_synth
+    inp = moe_synth.layer_inputs(wl, device=dev)
+    x, wr, w13, w2 = inp["x"], inp["w_router"], inp["w13"], inp["w2"]
+    g = torch.Generator(device=dev).manual_seed(99)
+    w13s = (torch.randn((2 * wl.F, wl.d), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    w2s = (torch.randn((wl.d, wl.F), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    o_serial = moe.forward_shared(x, wr, w13, w2, w13s, w2s, wl.k)
+    o_over = moe.forward_shared(x, wr, w13, w2, w13s, w2s, wl.k, side_stream=side)
+    y_mb = torch.empty_like(x)
+
+    def run(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return round(e0.elapsed_time(e1) / steps * 1e3, 1)
+
+    res = {"workload": f"{wl.name}: T={wl.T} d={wl.d} E={wl.E} k={wl.k} F={wl.F}, shared expert F={wl.F}"}
+    res["shared_serial_us"] = run(lambda: moe.forward_shared(x, wr, w13, w2, w13s, w2s, wl.k,
+                                                             out=o_serial))
+    res["shared_two_streams_us"] = run(lambda: moe.forward_shared(x, wr, w13, w2, w13s, w2s, wl.k,
+                                                                  side_stream=side, out=o_over))
+    res["whole_batch_us"] = run(lambda: moe.forward(x, wr, w13, w2, wl.k))
+    res["two_microbatches_two_streams_us"] = run(
+        lambda: moe.forward_microbatched(x, wr, w13, w2, wl.k, 2, streams=[main, side], y=y_mb))
+    del inp, o_serial, o_over
+    return res
+
+
 def cpu_baseline(wl, inp, target_s):
     """The oracle as it is, on the host cores, over whole passes of the workload."""
     import threadpoolctl
@@ -436,6 +480,11 @@ def main():
     moe.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only_overlap:
+        ov = overlap_bench(torch, moe, moe_synth.WORKLOADS["mid_bf16"], dev, args.steps,
+                           args.warmup)
+        print(json.dumps({"overlap": ov}), flush=True)
+        return
     if args.only_ep:
         ep = ep_bench(torch, moe, moe_synth.WORKLOADS["ep32_zipf"], dev, args.steps, args.warmup)
         print(json.dumps({"ep_dispatch_combine": ep}), flush=True)
@@ -492,6 +541,9 @@ def main():
         torch.cuda.empty_cache()
         line["ep_dispatch_combine"] = ep_bench(torch, moe, moe_synth.WORKLOADS["ep32_zipf"], dev,
                                                max(5, args.steps // 2), max(2, args.warmup // 2))
+        torch.cuda.empty_cache()
+        line["overlap"] = overlap_bench(torch, moe, wl, dev, max(5, args.steps // 2),
+                                        max(2, args.warmup // 2))
         if not args.no_large:
             lwl = moe_synth.WORKLOADS["large_bf16"]
             linp, lel, lst = forward_bench(torch, moe, lwl, dev, 5, 2)

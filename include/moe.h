@@ -236,6 +236,16 @@ moe_status_t moe_ep_recv_gather_fp8(const uint8_t *q_region, const float *scale_
 moe_status_t moe_ep_recv_scatter(const void *y_local, const int32_t *row_src, int64_t cap,
                                  int64_t d, moe_dtype_t dtype, void *y_region, void *stream);
 
+/* moe_combine_add: y[t,:] = residual[t,:] + sum_{j<k} topk_w[t,j] * y_disp[pair_slot[t,j], :]
+ * (the float32 sum starts from the residual, then the j-ordered fmas, one rounding).
+ * [EFA] Dispatch and combine: while the sender half of dispatch waits on the network
+ * the GPU computes other work such as the shared expert; this call adds that shared
+ * expert's output (residual [T,d] dtype, e.g. moe_expert_ffn with E = 1 on x) into the
+ * combine. y may alias neither y_disp nor residual. */
+moe_status_t moe_combine_add(const void *y_disp, const int32_t *pair_slot, const float *topk_w,
+                             int64_t T, int32_t k, int64_t d, int64_t rows_total,
+                             moe_dtype_t dtype, const void *residual, void *y, void *stream);
+
 /* ------------------------------------------------ partial combine (rank-major)
  * [EFA] Dispatch/combine latency: the article accumulates only at the receiver of the
  * combine. The variant here lets each destination of the rank-major layout first sum,

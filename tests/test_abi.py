@@ -149,3 +149,9 @@ def test_partial_combine_host_validation(lib):
     assert p(FAKE, FAKE, FAKE, 10, 2, 60, 4, 100, BF16, FAKE, None) == ALIGN
     assert q(FAKE, FAKE, 10, 2, 64, 0, 100, BF16, FAKE, None) == INVALID              # n_dst 0
     assert q(None, None, 0, 2, 64, 4, 100, BF16, None, None) == OK
+
+
+def test_combine_add_host_validation(lib):
+    a = lib.moe_combine_add
+    assert a(FAKE, FAKE, FAKE, 10, 2, 64, 20, BF16, None, FAKE, None) == INVALID     # residual
+    assert a(FAKE, FAKE, FAKE, 10, 2, 64, 20, BF16, FAKE + 8, FAKE, None) == ALIGN

@@ -22,7 +22,8 @@ __all__ = ["MoEError", "load", "library_path", "moe_abi_version", "moe_route", "
            "moe_expert_ffn_down", "moe_combine", "moe_combine_bwd",
            "moe_expert_ffn_bwd", "moe_route_bwd", "moe_dispatch_bwd", "moe_ep_recv_plan",
            "moe_ep_recv_gather", "moe_ep_recv_scatter", "moe_dispatch_fp8",
-           "moe_ep_recv_gather_fp8", "moe_combine_partial", "moe_combine_partials", "Layout", "forward",
+           "moe_ep_recv_gather_fp8", "moe_combine_partial", "moe_combine_partials", "moe_combine_add",
+           "forward_shared", "forward_microbatched", "Layout", "forward",
            "backward",
            "EXPORTED"]
 
@@ -62,6 +63,7 @@ EXPORTED = {
     "moe_dispatch_fp8": (_I32, [_P, _P, _I64, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
                                 _P, _SZ, _P]),
     "moe_ep_recv_gather_fp8": (_I32, [_P, _P, _P, _I64, _I64, _P, _P]),
+    "moe_combine_add": (_I32, [_P, _P, _P, _I64, _I32, _I64, _I64, _I32, _P, _P, _P]),
     "moe_combine_partial": (_I32, [_P, _P, _P, _I64, _I32, _I64, _I32, _I64, _I32, _P, _P]),
     "moe_combine_partials": (_I32, [_P, _P, _I64, _I32, _I64, _I32, _I64, _I32, _P, _P]),
     "moe_ep_recv_plan": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I64, _P, _P, _P]),
@@ -346,6 +348,18 @@ def moe_dispatch_bwd(dx_disp, pair_slot, *, topk_idx=None, dlogits_sel=None, w_r
     return dx
 
 
+def moe_combine_add(y_disp, pair_slot, topk_w, residual, *, y=None, stream=None):
+    """y[t] = residual[t] + sum_j topk_w[t,j] * y_disp[pair_slot[t,j]]."""
+    T, k = pair_slot.shape
+    rows, d = y_disp.shape
+    if y is None:
+        y = torch.empty((T, d), dtype=y_disp.dtype, device=y_disp.device)
+    _check("moe_combine_add", load().moe_combine_add(
+        _ptr(y_disp), _ptr(pair_slot), _ptr(topk_w), T, k, d, rows, _dt(y_disp), _ptr(residual),
+        _ptr(y), _stream(stream)))
+    return y
+
+
 def moe_combine_partial(y_disp, pair_slot, topk_w, n_dst: int, cap: int, *, partial=None,
                         stream=None):
     """Per (token, destination) gate-weighted partial sums [n_dst*T, d] (rank-major)."""
@@ -416,6 +430,72 @@ def moe_ep_recv_scatter(y_local, row_src, y_region, *, stream=None):
     _check("moe_ep_recv_scatter", load().moe_ep_recv_scatter(
         _ptr(y_local), _ptr(row_src), cap, d, _dt(y_local), _ptr(y_region), _stream(stream)))
     return y_region
+
+
+# ------------------------------------------------- overlap (two streams)
+def forward_shared(x, w_router, w13, w2, w13_shared, w2_shared, k: int, *, side_stream=None,
+                   out: Optional[dict] = None):
+    """The layer plus one shared expert (a SwiGLU applied to every token, here the grouped
+    GEMM with E = 1). The shared expert runs on `side_stream` while route, dispatch and the
+    routed experts run on the current stream; moe_combine_add then adds its output into
+    the combine ([EFA] Dispatch and combine: the dispatch's sender half returns and the
+    GPU does other work, such as the shared expert, while the transfer is in flight).
+    With side_stream None everything runs on the current stream, in the same order."""
+    T, d = x.shape
+    main = torch.cuda.current_stream()
+    side = side_stream if side_stream is not None else main
+    o = dict(out or {})
+    if o.get("shared_off") is None:
+        o["shared_off"] = torch.tensor([0, T], dtype=torch.int32, device=x.device)
+    if side is not main:
+        side.wait_stream(main)
+    with torch.cuda.stream(side):
+        shared = moe_expert_ffn(x, o["shared_off"], w13_shared.unsqueeze(0),
+                                w2_shared.unsqueeze(0), y_disp=o.get("shared"), stream=side)
+    idx, gates, _ = moe_route(x, w_router, k, topk_idx=o.get("topk_idx"), topk_w=o.get("topk_w"))
+    plan = moe_dispatch(x, idx, w_router.shape[0], out=o.get("plan"))
+    y_disp = moe_expert_ffn(plan["x_disp"], plan["expert_off"], w13, w2, y_disp=o.get("y_disp"),
+                            ws=o.get("ws"))
+    if side is not main:
+        main.wait_stream(side)
+        shared.record_stream(main)
+    y = moe_combine_add(y_disp, plan["pair_slot"], gates, shared, y=o.get("y"))
+    o.update(topk_idx=idx, topk_w=gates, plan=plan, y_disp=y_disp, shared=shared, y=y)
+    return o
+
+
+def forward_microbatched(x, w_router, w13, w2, k: int, n_micro: int = 2, *, streams=None,
+                         y=None):
+    """The layer on n_micro consecutive slices of the tokens, slice i on streams[i % len]
+    so that one slice's memory-bound steps overlap another's grouped GEMM ([EFA] the
+    dispatch and combine are split into halves to allow overlap and micro-batching).
+    Every token's result equals the whole-batch forward bit for bit."""
+    T, d = x.shape
+    main = torch.cuda.current_stream()
+    streams = streams or [main]
+    if y is None:
+        y = torch.empty((T, d), dtype=x.dtype, device=x.device)
+    bounds = [T * i // n_micro for i in range(n_micro + 1)]
+    for s in streams:
+        if s is not main:
+            s.wait_stream(main)
+    for i in range(n_micro):
+        s = streams[i % len(streams)]
+        a, b = bounds[i], bounds[i + 1]
+        if b == a:
+            continue
+        with torch.cuda.stream(s):
+            xi = x[a:b]
+            idx, gates, _ = moe_route(xi, w_router, k, stream=s)
+            plan = moe_dispatch(xi, idx, w_router.shape[0], stream=s)
+            y_disp = moe_expert_ffn(plan["x_disp"], plan["expert_off"], w13, w2, stream=s)
+            moe_combine(y_disp, plan["pair_slot"], gates, y=y[a:b], stream=s)
+            for t in (idx, gates, y_disp, *[v for v in plan.values() if v is not None]):
+                t.record_stream(s)
+    for s in streams:
+        if s is not main:
+            main.wait_stream(s)
+    return y
 
 
 # ------------------------------------------------------------ whole layer

@@ -20,6 +20,7 @@ __global__ __launch_bounds__(256) void k_combine(const uint4 *__restrict__ y_dis
                                                  const int *__restrict__ pair_slot,
                                                  const float *__restrict__ topk_w, int T, int k,
                                                  int rc, int64_t rows_total,
+                                                 const uint4 *__restrict__ residual,
                                                  uint4 *__restrict__ y) {
     constexpr int VN = Vec<DT>::N;
     const int lane = threadIdx.x & (kWave - 1);
@@ -30,8 +31,12 @@ __global__ __launch_bounds__(256) void k_combine(const uint4 *__restrict__ y_dis
         const float *pw = topk_w + size_t(t) * k;
         for (int c = lane; c < rc; c += kWave) {
             float acc[VN];
+            if (residual) {
+                Vec<DT>::unpack(residual[size_t(t) * rc + c], acc);   // the sum starts here
+            } else {
 #pragma unroll
-            for (int i = 0; i < VN; ++i) acc[i] = 0.0f;
+                for (int i = 0; i < VN; ++i) acc[i] = 0.0f;
+            }
             for (int j = 0; j < k; ++j) {
                 const int s = ps[j];
                 if (s < 0 || s >= rows_total) continue;
@@ -182,26 +187,45 @@ int row_grid(int64_t T) { return int(std::min<int64_t>(cdiv(T, 4), 8192)); }
 
 using namespace moe;
 
-extern "C" moe_status_t moe_combine(const void *y_disp, const int32_t *pair_slot,
-                                    const float *topk_w, int64_t T, int32_t k, int64_t d,
-                                    int64_t rows_total, moe_dtype_t dtype, void *y, void *stream) {
+namespace {
+moe_status_t combine_impl(const void *y_disp, const int32_t *pair_slot, const float *topk_w,
+                          int64_t T, int32_t k, int64_t d, int64_t rows_total, moe_dtype_t dtype,
+                          const void *residual, void *y, void *stream) {
     if (!valid_dtype(dtype) || T < 0 || d <= 0 || k <= 0 || rows_total < 0)
         return MOE_ERR_INVALID_ARG;
     if (T > (int64_t(1) << 31) / 64) return MOE_ERR_UNSUPPORTED;
     if (T == 0) return MOE_OK;
     if (!y_disp || !pair_slot || !topk_w || !y) return MOE_ERR_INVALID_ARG;
     const int64_t rowb = d * elt_size(dtype);
-    if (rowb % 16 != 0 || !aligned16(y_disp) || !aligned16(y)) return MOE_ERR_ALIGN;
+    if (rowb % 16 != 0 || !aligned16(y_disp) || !aligned16(y) || (residual && !aligned16(residual)))
+        return MOE_ERR_ALIGN;
     const hipStream_t st = as_stream(stream);
     if (dtype == MOE_BF16)
         hipLaunchKernelGGL(k_combine<MOE_BF16>, dim3(row_grid(T)), dim3(256), 0, st,
                            static_cast<const uint4 *>(y_disp), pair_slot, topk_w, int(T), k,
-                           int(rowb / 16), rows_total, static_cast<uint4 *>(y));
+                           int(rowb / 16), rows_total, static_cast<const uint4 *>(residual),
+                           static_cast<uint4 *>(y));
     else
         hipLaunchKernelGGL(k_combine<MOE_F32>, dim3(row_grid(T)), dim3(256), 0, st,
                            static_cast<const uint4 *>(y_disp), pair_slot, topk_w, int(T), k,
-                           int(rowb / 16), rows_total, static_cast<uint4 *>(y));
+                           int(rowb / 16), rows_total, static_cast<const uint4 *>(residual),
+                           static_cast<uint4 *>(y));
     return launch_status();
+}
+}  // namespace
+
+extern "C" moe_status_t moe_combine(const void *y_disp, const int32_t *pair_slot,
+                                    const float *topk_w, int64_t T, int32_t k, int64_t d,
+                                    int64_t rows_total, moe_dtype_t dtype, void *y, void *stream) {
+    return combine_impl(y_disp, pair_slot, topk_w, T, k, d, rows_total, dtype, nullptr, y, stream);
+}
+
+extern "C" moe_status_t moe_combine_add(const void *y_disp, const int32_t *pair_slot,
+                                        const float *topk_w, int64_t T, int32_t k, int64_t d,
+                                        int64_t rows_total, moe_dtype_t dtype, const void *residual,
+                                        void *y, void *stream) {
+    if (!residual) return MOE_ERR_INVALID_ARG;
+    return combine_impl(y_disp, pair_slot, topk_w, T, k, d, rows_total, dtype, residual, y, stream);
 }
 
 extern "C" moe_status_t moe_combine_bwd(const void *dy, const void *y_disp,
