@@ -34,6 +34,8 @@ METRIC = "MoE-layer tokens/s fwd(+bwd) on 1 MI355X; dispatch/combine GB/s; GEMM 
 PEAK_HBM_GBS = 8000.0          # HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
 PEAK_FP32_VALU_TFLOPS = 78.6   # fp32 FMA without packed-FP32 ops: 256 CU * 4 SIMD * 16 lanes * 2 * 2.4 GHz
+PEAK_FP32_MFMA_TFLOPS = 157.3  # dense fp32 MFMA
+PEAKS = {"mfma": PEAK_BF16_TFLOPS, "mfma_f32": PEAK_FP32_MFMA_TFLOPS, "valu": PEAK_FP32_VALU_TFLOPS}
 
 
 def parse():
@@ -66,8 +68,10 @@ def stage_work(wl):
     T, d, E, k, F = wl.T, wl.d, wl.E, wl.k, wl.F
     P = T * k
     return {
-        # x and the router weights read once; indices and gates written
-        "route": dict(bytes=T * d * b + E * d * b + P * 8, flops=2 * T * d * E, unit="valu"),
+        # x and the router weights read once; indices and gates written. bf16 logits run
+        # as float32 matrix-core chains, float32 ones on the vector ALU
+        "route": dict(bytes=T * d * b + E * d * b + P * 8, flops=2 * T * d * E,
+                      unit="mfma_f32" if wl.dtype == "bf16" else "valu"),
         # each token read once and written k times (the plan's int traffic is < 1 %)
         "dispatch": dict(bytes=T * d * b + P * d * b, flops=0, unit="hbm"),
         # every expert weight read once, dispatched rows read, a = silu(h)*u written
@@ -101,7 +105,7 @@ def bound_of(work):
     t_mem = work["bytes"] / (PEAK_HBM_GBS * 1e9)
     if work["flops"] == 0:
         return "hbm", t_mem
-    peak = PEAK_BF16_TFLOPS if work["unit"] == "mfma" else PEAK_FP32_VALU_TFLOPS
+    peak = PEAKS[work["unit"]]
     t_cmp = work["flops"] / (peak * 1e12)
     if work["unit"] == "hbm":
         return "hbm", t_mem
@@ -506,7 +510,7 @@ def main():
     if bound == "hbm":
         achieved, peak, unit, per = w["bytes"] / t / 1e9, PEAK_HBM_GBS, "GB/s", w["bytes"]
     else:
-        peak = PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_FP32_VALU_TFLOPS
+        peak = PEAKS[bound]
         achieved, unit, per = w["flops"] / t / 1e12, "TFLOP/s", w["flops"]
     roofline = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": measured_traffic(dom), "kernel": dom,

@@ -4,12 +4,24 @@
 // (Introduction); each token goes to R of E experts (Send and receive buffers).
 //
 // Logits: acc = fmaf(x[t,i], w[e,i], acc) for i = 0..d-1 from +0, float32. The
-// integer routing decision depends on these bits, so the order is fixed; that keeps
-// the contraction on the vector ALU (matrix cores accumulate in their own order).
-// The kernel is an LDS-tiled register-blocked product: a workgroup owns TT tokens and
-// all (padded) experts, each thread TM tokens x TE experts whose accumulation chains
-// each run over i in order. Top-k then runs on the logits tile held in LDS.
+// integer routing decision depends on these bits, so the order is fixed: every
+// output is one chain of d dependent multiply-adds, never split or reassociated.
+//
+// bf16 path (matrix cores): a product of two bf16 values is exact in float32 (8-bit
+// significands), so one float32 outer-product step D = C + a*b of
+// v_mfma_f32_4x4x1_16b_f32 (sixteen 4x4 blocks, one product per output) rounds
+// exactly as fmaf(a, b, C) does. Chaining those steps over i = 0..d-1 gives the
+// canonical logits bit for bit, with the multiply-adds on the matrix cores at twice
+// the vector-ALU rate; a chain advances one step per MFMA latency, so many
+// independent 16-token x 16-expert chains are kept in flight.
+// float32 path (vector ALU): products are not exact there, so the chains run as
+// v_fma_f32 in an LDS-tiled register-blocked kernel: a workgroup owns TT tokens and all
+// (padded) experts, each thread TM tokens x TE experts.
+// Both paths then run top-k on the workgroup's logits tile in LDS.
 #include "common.h"
+
+#include <algorithm>
+#include <mutex>
 
 namespace moe {
 namespace {
@@ -18,6 +30,74 @@ constexpr int kRouteBK = 32;      // input elements per LDS stage
 constexpr int kRouteThreads = 256;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Top-k and gates of the workgroup's rows of the logits tile lg[rows][SL] (LDS), one
+// wavefront per row; lane l holds experts l, l+64, ... (NV candidates per lane).
+template <int NV>
+__device__ __forceinline__ void topk_rows(const float *lg, int SL, int rows, int t0, int T, int E,
+                                          int k, int full_softmax, int *__restrict__ topk_idx,
+                                          float *__restrict__ topk_w, int wave, int lane,
+                                          int nwaves) {
+    for (int r = wave; r < rows; r += nwaves) {
+        const int t = t0 + r;
+        if (t >= T) break;
+        float v[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int e = lane + i * kWave;
+            v[i] = (e < E) ? lg[r * SL + e] : 0.0f;
+        }
+        uint32_t taken = 0;
+        int my_idx = 0;
+        float my_v = 0.0f;
+        for (int j = 0; j < k; ++j) {
+            float bv = 0.0f;
+            int bi = 0x7fffffff;           // "none"
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const int e = lane + i * kWave;
+                // ascending e and strict '>' keep the lower id on ties
+                if (e < E && !((taken >> i) & 1u) && (bi == 0x7fffffff || v[i] > bv)) {
+                    bv = v[i];
+                    bi = e;
+                }
+            }
+#pragma unroll
+            for (int off = kWave / 2; off > 0; off >>= 1) {
+                const float ov = __shfl_xor(bv, off, kWave);
+                const int oi = __shfl_xor(bi, off, kWave);
+                if (oi != 0x7fffffff &&
+                    (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) {
+                    bv = ov;
+                    bi = oi;
+                }
+            }
+            if (lane == j) {
+                my_idx = bi;
+                my_v = bv;
+            }
+            if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
+        }
+        const float vmax = __shfl(my_v, 0, kWave);   // the first pick is the largest
+        float z, s;
+        if (!full_softmax) {
+            z = (lane < k) ? expf(my_v - vmax) : 0.0f;
+            s = z;
+        } else {
+            z = (lane < k) ? expf(my_v - vmax) : 0.0f;
+            s = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                if (lane + i * kWave < E) s += expf(v[i] - vmax);
+        }
+#pragma unroll
+        for (int off = kWave / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, kWave);
+        if (lane < k) {
+            topk_idx[size_t(t) * k + lane] = my_idx;
+            topk_w[size_t(t) * k + lane] = z / s;
+        }
+    }
+}
 
 template <int DT, int TM, int TE>
 __global__ __launch_bounds__(kRouteThreads) void k_router_topk(
@@ -149,68 +229,176 @@ __global__ __launch_bounds__(kRouteThreads) void k_router_topk(
         }
     }
 
-    // top-k: one wavefront per token. Lane l holds experts l, l+64, ...
+    topk_rows<NV>(lg, SL, TT, t0, T, E, k, full_softmax, topk_idx, topk_w, tid / kWave,
+              tid & (kWave - 1), kRouteThreads / kWave);
+}
+
+// ---------------------------------------------------------------- bf16 matrix-core path
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRouteTT = 16;          // tokens per workgroup of the matrix-core path
+
+// Chain c of wave v covers tokens t0..t0+15 and experts e = 16*(NCH*v + c) .. +15.
+// MFMA 4x4x1_16b lane layout (block b = l >> 2): lane l supplies operand A of block b,
+// row l & 3, and operand B of block b, column l & 3; result register q of lane l is
+// block b, row q, column l & 3. Blocks are laid out as 4 token groups x 4 expert groups
+// (b = 4 * (l >> 4) + ((l >> 2) & 3)), so lane l feeds token t0 + 4*(l >> 4) + (l & 3)
+// and expert e + (l & 15), and ends holding the logits of tokens t0 + 4*(l >> 4) + q
+// for expert e + (l & 15).
+// Operands are staged in LDS as float32, BK elements of every row per stage (each
+// value widened once per workgroup: a vector-ALU op costs the matrix pipe about as
+// much as a step), and read 4 steps at a time; the raw bf16 rows of the next four
+// stages are in flight in registers meanwhile. Elements past the row end stage as
+// zeros: adding the product +0 leaves an accumulator unchanged (it is never -0: it
+// starts at +0 and round-to-nearest-even turns exact cancellation into +0), so every
+// chain is exactly the d-step chain.
+template <int NCH, int NV, int BK, int CPT>
+__global__ __launch_bounds__(512) void k_router_mfma(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, int T, int d, int E, int k,
+    int full_softmax, float *__restrict__ logits, int *__restrict__ topk_idx,
+    float *__restrict__ topk_w) {
+    constexpr int XP = BK + 4;                        // LDS row pitch (floats)
+    constexpr int CPR = BK / 8;                       // 16-byte chunks per row and stage
+    constexpr int PF = 4;                             // stages of raw rows in flight
+    extern __shared__ __align__(16) float smem[];
+    const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    for (int r = wave; r < TT; r += kRouteThreads / kWave) {
-        const int t = t0 + r;
-        if (t >= T) break;
-        float v[NV];
+    const int nwaves = blockDim.x / kWave;
+    const int ep = 16 * NCH * nwaves;                 // padded experts of the workgroup
+    const int rows = kRouteTT + ep;                   // staged rows: tokens, then experts
+    const int stage_floats = rows * XP;
+    const int t0 = blockIdx.x * kRouteTT;
+
+    // chunk c of a stage is row c / CPR, elements 8*(c % CPR) .. +7; thread tid owns
+    // chunks tid + j*blockDim (j < CPT; the host keeps rows*CPR <= CPT*blockDim)
+    const int nchunks = rows * CPR;
+    const uint16_t *src[CPT];
+    int coff[CPT];
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int e = lane + i * kWave;
-            v[i] = (e < E) ? lg[r * SL + e] : 0.0f;
-        }
-        uint32_t taken = 0;
-        int my_idx = 0;
-        float my_v = 0.0f;
-        for (int j = 0; j < k; ++j) {
-            float bv = 0.0f;
-            int bi = 0x7fffffff;           // "none"
+    for (int j = 0; j < CPT; ++j) {
+        const int c = min(tid + j * int(blockDim.x), nchunks - 1);
+        const int r = c / CPR;
+        src[j] = (r < kRouteTT) ? x + size_t(min(t0 + r, T - 1)) * d
+                                : w + size_t(min(r - kRouteTT, E - 1)) * d;
+        coff[j] = 8 * (c % CPR);
+    }
+    // raw rows of PF stages in registers; loads are unconditional (clamped inside the
+    // row) so the count in flight is the same at every wait, and the elements past d
+    // are zeroed when staged
+    uint4 raw[PF][CPT];
+    auto fetch = [&](int sidx, uint4 (&dst)[CPT]) {
 #pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                const int e = lane + i * kWave;
-                // ascending e and strict '>' keep the lower id on ties
-                if (e < E && !((taken >> i) & 1u) && (bi == 0x7fffffff || v[i] > bv)) {
-                    bv = v[i];
-                    bi = e;
-                }
+        for (int j = 0; j < CPT; ++j)
+            dst[j] = *reinterpret_cast<const uint4 *>(src[j] + min(sidx * BK + coff[j], d - 8));
+    };
+    auto stage = [&](int sidx, const uint4 (&v)[CPT], float *buf) {
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            const int c = tid + j * int(blockDim.x);
+            if (c < nchunks) {
+                const int r = c / CPR;
+                const bool in = sidx * BK + coff[j] < d;
+                const uint4 u = in ? v[j] : make_uint4(0u, 0u, 0u, 0u);
+                float4 *dst = reinterpret_cast<float4 *>(buf + r * XP + coff[j]);
+                dst[0] = make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
+                dst[1] = make_float4(bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w));
             }
-#pragma unroll
-            for (int off = kWave / 2; off > 0; off >>= 1) {
-                const float ov = __shfl_xor(bv, off, kWave);
-                const int oi = __shfl_xor(bi, off, kWave);
-                if (oi != 0x7fffffff &&
-                    (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) {
-                    bv = ov;
-                    bi = oi;
-                }
-            }
-            if (lane == j) {
-                my_idx = bi;
-                my_v = bv;
-            }
-            if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
         }
-        const float vmax = __shfl(my_v, 0, kWave);   // the first pick is the largest
-        float z, s;
-        if (!full_softmax) {
-            z = (lane < k) ? expf(my_v - vmax) : 0.0f;
-            s = z;
-        } else {
-            z = (lane < k) ? expf(my_v - vmax) : 0.0f;
-            s = 0.0f;
+    };
+
+    const int arow = 4 * (lane >> 4) + (lane & 3);
+    int brow[NCH];
 #pragma unroll
-            for (int i = 0; i < NV; ++i)
-                if (lane + i * kWave < E) s += expf(v[i] - vmax);
-        }
+    for (int c = 0; c < NCH; ++c) brow[c] = kRouteTT + 16 * (NCH * wave + c) + (lane & 15);
+
+    f32x4 acc[NCH];
 #pragma unroll
-        for (int off = kWave / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, kWave);
-        if (lane < k) {
-            topk_idx[size_t(t) * k + lane] = my_idx;
-            topk_w[size_t(t) * k + lane] = z / s;
+    for (int c = 0; c < NCH; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // stages rounded up to a multiple of PF: the extra stages are all zeros (no-op
+    // steps), which keeps the loop body free of conditions and every wait exact
+    const int nst = (d + BK * PF - 1) / (BK * PF) * PF;
+#pragma unroll
+    for (int p = 0; p < PF; ++p) fetch(p, raw[p]);
+    stage(0, raw[0], smem);
+    fetch(PF, raw[0]);
+    __syncthreads();
+    // stage s: the chains consume LDS buffer s & 1; raw slot (s+1) % PF is widened into
+    // the other buffer and refilled with stage s+1+PF
+    for (int s0 = 0; s0 < nst; s0 += PF) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+            const int s = s0 + u;
+            const float *cur = smem + (s & 1) * stage_floats;
+#pragma unroll
+            for (int kk = 0; kk < BK; kk += 4) {
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(cur + arow * XP + kk);
+                f32x4 b[NCH];
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) b[c] = *reinterpret_cast<const f32x4 *>(cur + brow[c] * XP + kk);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int c = 0; c < NCH; ++c)
+                        acc[c] = __builtin_amdgcn_mfma_f32_4x4x1f32(a[q], b[c][q], acc[c], 0, 0, 0);
+            }
+            stage(s + 1, raw[(u + 1) % PF], smem + ((s + 1) & 1) * stage_floats);
+            fetch(s + 1 + PF, raw[(u + 1) % PF]);
+            __syncthreads();
         }
     }
+
+    // logits tile -> LDS (the staging area is free after the last barrier)
+    const int SL = ep + 1;
+    float *lg = smem;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            lg[(4 * (lane >> 4) + q) * SL + 16 * (NCH * wave + c) + (lane & 15)] = acc[c][q];
+    __syncthreads();
+
+    if (logits != nullptr) {
+        for (int c = tid; c < kRouteTT * E; c += blockDim.x) {
+            const int r = c / E, e = c % E;
+            if (t0 + r < T) logits[size_t(t0 + r) * E + e] = lg[r * SL + e];
+        }
+    }
+    topk_rows<NV>(lg, SL, kRouteTT, t0, T, E, k, full_softmax, topk_idx, topk_w, wave, lane,
+                  nwaves);
+}
+
+template <int NCH, int NV, int BK, int CPT>
+moe_status_t launch_route_mfma_cfg(const uint16_t *x, const uint16_t *w, int T, int d, int E, int k,
+                                   int full, float *logits, int *idx, float *gw, hipStream_t st) {
+    // enough waves for the experts, and for the staging chunks (CPT per thread)
+    int nw = int(cdiv(E, 16 * NCH));
+    while (size_t(kRouteTT + 16 * NCH * nw) * (BK / 8) > size_t(CPT * 64 * nw) && nw < 8) ++nw;
+    const int ep = 16 * NCH * nw;
+    const size_t stage = size_t(kRouteTT + ep) * (BK + 4) * sizeof(float);
+    const size_t lds = std::max(2 * stage, size_t(kRouteTT) * (ep + 1) * sizeof(float));
+    if (size_t(kRouteTT + ep) * (BK / 8) > size_t(CPT * 64 * nw)) return MOE_ERR_UNSUPPORTED;
+    static std::once_flag once;
+    static bool lds_ok = false;
+    std::call_once(once, [] {
+        lds_ok = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_router_mfma<NCH, NV, BK, CPT>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess;
+    });
+    if (!lds_ok) return MOE_ERR_HIP;
+    hipLaunchKernelGGL((k_router_mfma<NCH, NV, BK, CPT>), dim3(unsigned(cdiv(T, kRouteTT))), dim3(64 * nw),
+                       lds, st, x, w, T, d, E, k, full, logits, idx, gw);
+    return launch_status();
+}
+
+moe_status_t launch_route_mfma(const void *x, const void *w, int T, int d, int E, int k, int full,
+                               float *logits, int *idx, float *gw, hipStream_t st) {
+    const auto xb = static_cast<const uint16_t *>(x);
+    const auto wb = static_cast<const uint16_t *>(w);
+    // one 16-expert chain per wave for small layers (the most chains in flight), four
+    // per wave (64 experts) for larger ones
+    if (E <= 64) return launch_route_mfma_cfg<1, 1, 64, 3>(xb, wb, T, d, E, k, full, logits, idx, gw, st);
+    return launch_route_mfma_cfg<4, 8, 16, 3>(xb, wb, T, d, E, k, full, logits, idx, gw, st);
 }
 
 template <int DT, int TM>
@@ -262,8 +450,8 @@ extern "C" moe_status_t moe_route(const void *x, const void *w_router, int64_t T
         return MOE_ERR_ALIGN;
     const hipStream_t st = as_stream(stream);
     if (dtype == MOE_BF16)
-        return launch_route<MOE_BF16>(x, w_router, int(T), int(d), E, k, flags, logits, topk_idx,
-                                      topk_w, st);
+        return launch_route_mfma(x, w_router, int(T), int(d), E, k, flags, logits, topk_idx, topk_w,
+                                 st);
     return launch_route<MOE_F32>(x, w_router, int(T), int(d), E, k, flags, logits, topk_idx,
                                  topk_w, st);
 }
