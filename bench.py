@@ -103,12 +103,9 @@ def bwd_work(wl):
 def bound_of(work):
     """hbm or mfma/valu: whichever lower bound on the time is larger."""
     t_mem = work["bytes"] / (PEAK_HBM_GBS * 1e9)
-    if work["flops"] == 0:
+    if work["flops"] == 0 or work["unit"] == "hbm":
         return "hbm", t_mem
-    peak = PEAKS[work["unit"]]
-    t_cmp = work["flops"] / (peak * 1e12)
-    if work["unit"] == "hbm":
-        return "hbm", t_mem
+    t_cmp = work["flops"] / (PEAKS[work["unit"]] * 1e12)
     return (work["unit"] if t_cmp >= t_mem else "hbm"), max(t_cmp, t_mem)
 
 

@@ -252,7 +252,7 @@ constexpr int kRouteTT = 16;          // tokens per workgroup of the matrix-core
 // zeros: adding the product +0 leaves an accumulator unchanged (it is never -0: it
 // starts at +0 and round-to-nearest-even turns exact cancellation into +0), so every
 // chain is exactly the d-step chain.
-template <int NCH, int NV, int BK, int CPT>
+template <int NCH, int NV, int BK, int CPTW>
 __global__ __launch_bounds__(512) void k_router_mfma(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, int T, int d, int E, int k,
     int full_softmax, float *__restrict__ logits, int *__restrict__ topk_idx,
@@ -260,50 +260,69 @@ __global__ __launch_bounds__(512) void k_router_mfma(
     constexpr int XP = BK + 4;                        // LDS row pitch (floats)
     constexpr int CPR = BK / 8;                       // 16-byte chunks per row and stage
     constexpr int PF = 4;                             // stages of raw rows in flight
+    constexpr int NL = 1 + CPTW;                      // loads per thread and stage
     extern __shared__ __align__(16) float smem[];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    const int nwaves = blockDim.x / kWave;
+    const int nthreads = int(blockDim.x);
+    const int nwaves = nthreads / kWave;
     const int ep = 16 * NCH * nwaves;                 // padded experts of the workgroup
     const int rows = kRouteTT + ep;                   // staged rows: tokens, then experts
     const int stage_floats = rows * XP;
     const int t0 = blockIdx.x * kRouteTT;
 
-    // chunk c of a stage is row c / CPR, elements 8*(c % CPR) .. +7; thread tid owns
-    // chunks tid + j*blockDim (j < CPT; the host keeps rows*CPR <= CPT*blockDim)
-    const int nchunks = rows * CPR;
-    const uint16_t *src[CPT];
-    int coff[CPT];
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-        const int c = min(tid + j * int(blockDim.x), nchunks - 1);
-        const int r = c / CPR;
-        src[j] = (r < kRouteTT) ? x + size_t(min(t0 + r, T - 1)) * d
-                                : w + size_t(min(r - kRouteTT, E - 1)) * d;
-        coff[j] = 8 * (c % CPR);
+    // Chunk = 8 elements of one row. Load 0 of a thread is token chunk tid % (16*CPR)
+    // (staged by threads < 16*CPR only); loads 1.. are expert chunks tid + j*nthreads
+    // (the host makes ep*CPR == CPTW*nthreads). Buffer loads: per-chunk row offset in
+    // the lane, stage offset uniform; a read past a row end lands in the next row (or
+    // reads zeros past the buffer) and is zeroed when staged.
+    const int xc = tid % (kRouteTT * CPR);
+    const bool xown = tid < kRouteTT * CPR;
+    const int64_t xrem = (int64_t(T) - t0) * d * 2;   // bytes from the tile's first row on
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(x + size_t(t0) * d), 0, int(xrem < 0x7fffffff ? xrem : 0x7fffffff), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(w), 0, int(int64_t(E) * d * 2), 0x00020000);
+    uint32_t voff[NL];
+    int lofs[NL], coff[NL];
+    {
+        const int r = xc / CPR;
+        coff[0] = 8 * (xc % CPR);
+        voff[0] = uint32_t((min(t0 + r, T - 1) - t0) * d + coff[0]) * 2u;
+        lofs[0] = r * XP + coff[0];
     }
-    // raw rows of PF stages in registers; loads are unconditional (clamped inside the
-    // row) so the count in flight is the same at every wait, and the elements past d
-    // are zeroed when staged
-    uint4 raw[PF][CPT];
-    auto fetch = [&](int sidx, uint4 (&dst)[CPT]) {
 #pragma unroll
-        for (int j = 0; j < CPT; ++j)
-            dst[j] = *reinterpret_cast<const uint4 *>(src[j] + min(sidx * BK + coff[j], d - 8));
+    for (int j = 0; j < CPTW; ++j) {
+        const int c = tid + j * nthreads;
+        const int r = c / CPR;
+        coff[1 + j] = 8 * (c % CPR);
+        voff[1 + j] = uint32_t(min(r, E - 1) * d + coff[1 + j]) * 2u;
+        lofs[1 + j] = (kRouteTT + r) * XP + coff[1 + j];
+    }
+    uint4 raw[PF][NL];
+    auto fetch = [&](int sidx, uint4 (&dst)[NL]) {
+        const int so = sidx * BK * 2;
+        dst[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff[0], so, 0));
+#pragma unroll
+        for (int j = 1; j < NL; ++j)
+            dst[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, voff[j], so, 0));
     };
-    auto stage = [&](int sidx, const uint4 (&v)[CPT], float *buf) {
+    auto cvt_store = [&](float *buf, int lo, uint4 u) {
+        float4 *dst = reinterpret_cast<float4 *>(buf + lo);
+        dst[0] = make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
+        dst[1] = make_float4(bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w));
+    };
+    auto stage = [&](int sidx, const uint4 (&v)[NL], float *buf) {
+        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+        if ((sidx + 1) * BK <= d) {                    // the whole stage is inside the rows
+            if (xown) cvt_store(buf, lofs[0], v[0]);
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            const int c = tid + j * int(blockDim.x);
-            if (c < nchunks) {
-                const int r = c / CPR;
-                const bool in = sidx * BK + coff[j] < d;
-                const uint4 u = in ? v[j] : make_uint4(0u, 0u, 0u, 0u);
-                float4 *dst = reinterpret_cast<float4 *>(buf + r * XP + coff[j]);
-                dst[0] = make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
-                dst[1] = make_float4(bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w));
-            }
+            for (int j = 1; j < NL; ++j) cvt_store(buf, lofs[j], v[j]);
+        } else {
+            if (xown) cvt_store(buf, lofs[0], sidx * BK + coff[0] < d ? v[0] : z);
+#pragma unroll
+            for (int j = 1; j < NL; ++j) cvt_store(buf, lofs[j], sidx * BK + coff[j] < d ? v[j] : z);
         }
     };
 
@@ -331,20 +350,37 @@ __global__ __launch_bounds__(512) void k_router_mfma(
         for (int u = 0; u < PF; ++u) {
             const int s = s0 + u;
             const float *cur = smem + (s & 1) * stage_floats;
+            // operands of group g (4 steps) are read RA groups ahead of its MFMAs
+            constexpr int NG = BK / 4, RA = NG < 4 ? NG : 4;
+            f32x4 a[RA], b[RA][NCH];
+            auto rd = [&](int g, f32x4 &ar, f32x4 (&br)[NCH]) {
+                ar = *reinterpret_cast<const f32x4 *>(cur + arow * XP + 4 * g);
 #pragma unroll
-            for (int kk = 0; kk < BK; kk += 4) {
-                const f32x4 a = *reinterpret_cast<const f32x4 *>(cur + arow * XP + kk);
-                f32x4 b[NCH];
+                for (int c = 0; c < NCH; ++c) br[c] = *reinterpret_cast<const f32x4 *>(cur + brow[c] * XP + 4 * g);
+            };
 #pragma unroll
-                for (int c = 0; c < NCH; ++c) b[c] = *reinterpret_cast<const f32x4 *>(cur + brow[c] * XP + kk);
+            for (int g = 0; g < RA; ++g) rd(g, a[g], b[g]);
+            __builtin_amdgcn_sched_barrier(0);
+            // (scheduling barriers keep every read RA groups ahead of its use)
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const f32x4 ag = a[g % RA];
+                f32x4 bg[NCH];
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) bg[c] = b[g % RA][c];
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
 #pragma unroll
                     for (int c = 0; c < NCH; ++c)
-                        acc[c] = __builtin_amdgcn_mfma_f32_4x4x1f32(a[q], b[c][q], acc[c], 0, 0, 0);
+                        acc[c] = __builtin_amdgcn_mfma_f32_4x4x1f32(ag[q], bg[c][q], acc[c], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                if (g + RA < NG) rd(g + RA, a[g % RA], b[g % RA]);
+                __builtin_amdgcn_sched_barrier(0);
             }
             stage(s + 1, raw[(u + 1) % PF], smem + ((s + 1) & 1) * stage_floats);
+            __builtin_amdgcn_sched_barrier(0);   // the loads keep their place in issue order
             fetch(s + 1 + PF, raw[(u + 1) % PF]);
+            __builtin_amdgcn_sched_barrier(0);
             __syncthreads();
         }
     }
@@ -369,25 +405,27 @@ __global__ __launch_bounds__(512) void k_router_mfma(
                   nwaves);
 }
 
-template <int NCH, int NV, int BK, int CPT>
+template <int NCH, int NV, int BK, int CPTW>
 moe_status_t launch_route_mfma_cfg(const uint16_t *x, const uint16_t *w, int T, int d, int E, int k,
-                                   int full, float *logits, int *idx, float *gw, hipStream_t st) {
-    // enough waves for the experts, and for the staging chunks (CPT per thread)
-    int nw = int(cdiv(E, 16 * NCH));
-    while (size_t(kRouteTT + 16 * NCH * nw) * (BK / 8) > size_t(CPT * 64 * nw) && nw < 8) ++nw;
+                                   int full, float *logits, int *idx, float *gw, hipStream_t st,
+                                   int nw) {
     const int ep = 16 * NCH * nw;
+    // every thread owns CPTW expert chunks, the first 16*CPR threads one token chunk
+    if (ep * (BK / 8) != CPTW * 64 * nw || kRouteTT * (BK / 8) > 64 * nw) return MOE_ERR_UNSUPPORTED;
+    // buffer offsets are 32-bit: the expert rows below 2^31 bytes, 16 token rows plus a
+    // stage offset well below 2^32
+    if (int64_t(E) * d * 2 > 0x7fffffff || d > (1 << 26)) return MOE_ERR_UNSUPPORTED;
     const size_t stage = size_t(kRouteTT + ep) * (BK + 4) * sizeof(float);
     const size_t lds = std::max(2 * stage, size_t(kRouteTT) * (ep + 1) * sizeof(float));
-    if (size_t(kRouteTT + ep) * (BK / 8) > size_t(CPT * 64 * nw)) return MOE_ERR_UNSUPPORTED;
     static std::once_flag once;
     static bool lds_ok = false;
     std::call_once(once, [] {
-        lds_ok = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_router_mfma<NCH, NV, BK, CPT>),
+        lds_ok = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_router_mfma<NCH, NV, BK, CPTW>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess;
     });
     if (!lds_ok) return MOE_ERR_HIP;
-    hipLaunchKernelGGL((k_router_mfma<NCH, NV, BK, CPT>), dim3(unsigned(cdiv(T, kRouteTT))), dim3(64 * nw),
-                       lds, st, x, w, T, d, E, k, full, logits, idx, gw);
+    hipLaunchKernelGGL((k_router_mfma<NCH, NV, BK, CPTW>), dim3(unsigned(cdiv(T, kRouteTT))),
+                       dim3(64 * nw), lds, st, x, w, T, d, E, k, full, logits, idx, gw);
     return launch_status();
 }
 
@@ -397,8 +435,10 @@ moe_status_t launch_route_mfma(const void *x, const void *w, int T, int d, int E
     const auto wb = static_cast<const uint16_t *>(w);
     // one 16-expert chain per wave for small layers (the most chains in flight), four
     // per wave (64 experts) for larger ones
-    if (E <= 64) return launch_route_mfma_cfg<1, 1, 64, 3>(xb, wb, T, d, E, k, full, logits, idx, gw, st);
-    return launch_route_mfma_cfg<4, 8, 16, 3>(xb, wb, T, d, E, k, full, logits, idx, gw, st);
+    if (E <= 64)   // four waves (64 padded experts), 128-deep stages
+        return launch_route_mfma_cfg<1, 1, 128, 4>(xb, wb, T, d, E, k, full, logits, idx, gw, st, 4);
+    return launch_route_mfma_cfg<4, 8, 16, 2>(xb, wb, T, d, E, k, full, logits, idx, gw, st,
+                                              int(cdiv(E, 64)));
 }
 
 template <int DT, int TM>
