@@ -14,7 +14,8 @@
 //                 whose result does not depend on the order); popcounts are the
 //                 block's per-expert counts.
 //   k_plan_scan   one workgroup: per-source counts, expert offsets, chunk offsets
-//                 per destination, and the first row of every (block, expert).
+//                 per destination, and the first row of every (block, expert);
+//                 k_plan_scan_em is the short form for the expert-major layout.
 //   k_plan_slots_copy  rebuilds the masks; a pair's rank inside its expert is the
 //                 popcount of the mask bits below its token, so tokens keep their
 //                 order inside every expert; marks unused rows with -1; then copies:
@@ -233,6 +234,73 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_scan(
         blk_base[i] = int(int64_t(r) * g.cap) + chk[r * (ns + 1) + s] + cnt[s * E + e] +
                       bct[(s * E + e) * bps + bb];
     }
+}
+
+// The plan's scan for the expert-major layout (one source, one destination): thread
+// e sums expert e's block counts, the experts' totals are scanned across the
+// workgroup, and a second walk over the counts writes the first row of every
+// (block, e) in block order. Counts are read 32 at a time (independent loads).
+__global__ __launch_bounds__(kScanThreads) void k_plan_scan_em(
+    const int *__restrict__ blk_counts, const int *__restrict__ blk_flags, PlanGeom g,
+    int *__restrict__ counts, int *__restrict__ expert_off, int *__restrict__ chunk_off,
+    int *__restrict__ blk_base, int *__restrict__ flag) {
+    constexpr int kBatch = 32;
+    __shared__ int wsum[kScanThreads / kWave];
+    __shared__ int sflag;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int E = g.E;
+    if (tid == 0) sflag = 0;
+    __syncthreads();
+    int fl = 0;
+    for (int b = tid; b < g.B; b += kScanThreads) fl |= blk_flags[b];
+    if (fl) atomicOr(&sflag, fl);
+    int tot = 0;
+    if (tid < E) {
+        for (int b0 = 0; b0 < g.B; b0 += kBatch) {
+            int c[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u)
+                c[u] = (b0 + u < g.B) ? blk_counts[size_t(b0 + u) * E + tid] : 0;
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) tot += c[u];
+        }
+        counts[tid] = tot;
+    }
+    // exclusive scan of the totals over e = tid
+    int v = tot;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(v, off, kWave);
+        if (lane >= off) v += o;
+    }
+    if (lane == kWave - 1) wsum[wave] = v;
+    __syncthreads();
+    int carry = 0;
+    for (int w = 0; w < wave; ++w) carry += wsum[w];
+    const int off_e = carry + v - tot;
+    if (tid < E) {
+        expert_off[tid] = off_e;
+        int run = off_e;
+        for (int b0 = 0; b0 < g.B; b0 += kBatch) {
+            int c[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u)
+                c[u] = (b0 + u < g.B) ? blk_counts[size_t(b0 + u) * E + tid] : 0;
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                if (b0 + u < g.B) blk_base[size_t(b0 + u) * E + tid] = run;
+                run += c[u];
+            }
+        }
+    }
+    if (tid == E - 1) {
+        expert_off[E] = off_e + tot;
+        chunk_off[0] = 0;
+        chunk_off[1] = off_e + tot;
+        if (int64_t(off_e + tot) > g.cap) atomicOr(&sflag, kFlagCapacity);
+    }
+    __syncthreads();
+    if (tid == 0) *flag = sflag;      // overwrites the previous call's flag
 }
 
 // Slots, unused-row marking and the copy, fused. Workgroup (b, q) rebuilds the masks
@@ -487,8 +555,12 @@ moe_status_t dispatch_impl(const void *x, const int32_t *topk_idx, int64_t T, in
 
     hipLaunchKernelGGL(k_plan_count, dim3(g.B), dim3(kPlanBlock), lds_mask, st, topk_idx, g,
                        blk_counts, blk_flags);
-    hipLaunchKernelGGL(k_plan_scan, dim3(1), dim3(kScanThreads), lds_scan, st, blk_counts,
-                       blk_flags, g, counts, expert_off, chunk_off, blk_base, flag);
+    if (n_src == 1 && n_dst == 1 && g.B <= 256)
+        hipLaunchKernelGGL(k_plan_scan_em, dim3(1), dim3(kScanThreads), 0, st, blk_counts,
+                           blk_flags, g, counts, expert_off, chunk_off, blk_base, flag);
+    else
+        hipLaunchKernelGGL(k_plan_scan, dim3(1), dim3(kScanThreads), lds_scan, st, blk_counts,
+                           blk_flags, g, counts, expert_off, chunk_off, blk_base, flag);
     if (q8)
         hipLaunchKernelGGL(k_plan_slots_copy<true>, dim3(g.B * kSubPerBlock), dim3(kCopyThreads),
                            lds_mask, st, topk_idx, g, blk_base, chunk_off, pair_slot, row_pair, flag,
