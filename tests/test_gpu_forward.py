@@ -41,6 +41,10 @@ ROUTE_CASES = [
     ("mid_bf16", dict(T=257, d=136, E=5, k=5)),       # k = E, d not a multiple of 32
     ("mid_bf16", dict(T=64, d=64, E=512, k=32)),      # largest E and k
     ("mid_bf16", dict(T=40, d=64, E=1, k=1)),
+    ("mid_bf16", dict(T=100, d=8, E=16, k=2)),       # one 16-byte piece per row
+    ("mid_bf16", dict(T=100, d=264, E=65, k=4)),     # just past one 64-expert group
+    ("mid_bf16", dict(T=37, d=520, E=128, k=8)),     # d % 128 != 0, two expert groups
+    ("mid_bf16", {}),                                # the full T=4096 router, logits too
 ]
 
 
