@@ -92,8 +92,9 @@ const char *moe_status_str(moe_status_t status);
  *   reading that makes the gate-weighted average of combine a true average.
  *
  * x [T,d] dtype, w_router [E,d] dtype; logits [T,E] f32 (NULL: not written);
- * topk_idx [T,k] int32; topk_w [T,k] f32. Limits: 1 <= k <= min(E, 32), E <= 512.
- * T = 0 is a no-op. */
+ * topk_idx [T,k] int32; topk_w [T,k] f32. Limits: 1 <= k <= min(E, 32), E <= 512;
+ * for bf16 also d <= 2^26 and E*d*2 < 2^31 bytes (32-bit buffer offsets), else
+ * MOE_ERR_UNSUPPORTED before anything is launched. T = 0 is a no-op. */
 moe_status_t moe_route(const void *x, const void *w_router, int64_t T, int64_t d, int32_t E,
                        int32_t k, moe_dtype_t dtype, int32_t flags, float *logits,
                        int32_t *topk_idx, float *topk_w, void *stream);

@@ -54,6 +54,10 @@ def test_route_host_validation(lib):
     assert r(FAKE, FAKE, 10, 64, 8, 2, BF16, 5, None, FAKE, FAKE, None) == INVALID    # flags
     assert r(FAKE, FAKE, 10, 60, 8, 2, BF16, 0, None, FAKE, FAKE, None) == ALIGN      # 120 B rows
     assert r(FAKE + 8, FAKE, 10, 64, 8, 2, BF16, 0, None, FAKE, FAKE, None) == ALIGN
+    # bf16 buffer offsets are 32-bit: rows beyond 2^26 elements, or router weights of
+    # 2^31 bytes, are refused before any launch
+    assert r(FAKE, FAKE, 10, (1 << 26) + 8, 8, 2, BF16, 0, None, FAKE, FAKE, None) == UNSUPPORTED
+    assert r(FAKE, FAKE, 10, 1 << 22, 512, 2, BF16, 0, None, FAKE, FAKE, None) == UNSUPPORTED
     assert r(None, FAKE, 10, 64, 8, 2, BF16, 0, None, FAKE, FAKE, None) == INVALID
     assert r(FAKE, FAKE, 10, 64, 600, 2, BF16, 0, None, FAKE, FAKE, None) == UNSUPPORTED
     assert r(FAKE, FAKE, 10, 64, 64, 33, BF16, 0, None, FAKE, FAKE, None) == UNSUPPORTED
