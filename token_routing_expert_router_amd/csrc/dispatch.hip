@@ -308,7 +308,7 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_scan_em(
 // then copies those tokens: one wavefront per token reads the row once with 16-byte
 // loads and writes it to each of its k rows. All workgroups together also mark the
 // rows no pair uses with row_pair = -1.
-constexpr int kSubTokens = 32;
+constexpr int kSubTokens = 16;
 constexpr int kSubPerBlock = kPlanBlock / kSubTokens;
 
 // Block-scaled fp8 payload of 16 consecutive elements (two 16-byte chunks of bf16) of
