@@ -127,6 +127,20 @@ def topk_gating(logits: np.ndarray, k: int, renorm: bool = True):
     return idx, gates
 
 
+def topk_gap(logits: np.ndarray, k: int) -> np.ndarray:
+    """Per token, the gap between its k-th and (k+1)-th largest logit (float64; +inf
+    when k == E). A token whose gap is below the rounding error of a reordered sum
+    could change its selection if the logits were summed in another order, which is
+    why the router fixes one order (the near-tie audit counts such tokens)."""
+    logits = np.asarray(logits, dtype=np.float64)
+    T, E = logits.shape
+    assert 1 <= k <= E
+    if k == E:
+        return np.full(T, np.inf)
+    srt = -np.sort(-logits, axis=1)
+    return srt[:, k - 1] - srt[:, k]
+
+
 def route(x, w_router, k: int, renorm: bool = True):
     logits = router_logits(x, w_router)
     idx, gates = topk_gating(logits, k, renorm)

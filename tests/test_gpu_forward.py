@@ -208,7 +208,14 @@ def test_mid_bf16_full_forward(gpu_lib):
     torch.cuda.synchronize()
     host = {n: t.cpu() for n, t in inp.items()}
     ref = oracle.forward(host["x"], host["w_router"], host["w13"], host["w2"], wl.k)
-    assert np.array_equal(out["topk_idx"].cpu().numpy(), ref["idx"])
+    got_idx = out["topk_idx"].cpu().numpy()
+    # near-tie audit: tokens whose k-th and (k+1)-th logits are closer than a
+    # reordered sum's rounding error keep their oracle selection too
+    gap = oracle.topk_gap(oracle.router_logits(host["x"], host["w_router"]), wl.k)
+    near = np.nonzero(gap < 1e-4)[0]
+    _say(f"  near-tie audit: {near.size} tokens with gap < 1e-4 (min gap {gap.min():.3g})")
+    assert np.array_equal(got_idx[near], ref["idx"][near])
+    assert np.array_equal(got_idx, ref["idx"])
     for key in ("counts", "expert_off", "pair_slot", "row_pair"):
         assert np.array_equal(out[key].cpu().numpy().reshape(ref[key].shape), ref[key]), key
     e_y = oracle.normwise_rel_err(_np(out["y"]), ref["y"])

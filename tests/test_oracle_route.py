@@ -120,3 +120,17 @@ def test_gates_are_renormalised_full_softmax():
     full /= full.sum(axis=1, keepdims=True)
     assert np.allclose(g_full, np.take_along_axis(full, idx, 1), rtol=1e-13, atol=0)
     assert np.allclose(g_renorm, g_full / g_full.sum(axis=1, keepdims=True), rtol=1e-13, atol=0)
+
+
+def test_topk_gap_brute_force():
+    """The k/(k+1) gap against an explicit enumeration of every logit's rank."""
+    rng = np.random.default_rng(7)
+    lg = rng.normal(0, 1, (50, 9)).astype(np.float32)
+    lg[3, 2] = lg[3, 5]                      # an exact tie straddling the cut for some k
+    for k in (1, 3, 8, 9):
+        gap = oracle.topk_gap(lg, k)
+        for t in range(lg.shape[0]):
+            vals = sorted((float(v) for v in lg[t]), reverse=True)
+            want = np.inf if k == lg.shape[1] else vals[k - 1] - vals[k]
+            assert gap[t] == want, (t, k)
+    assert np.all(oracle.topk_gap(lg, 3) >= 0)
