@@ -110,15 +110,22 @@ __device__ void seg_exclusive_scan(int *a, int n, int L, int *seg_total, int *wf
     const int per = (n + kScanThreads - 1) / kScanThreads;
     const int lo = min(n, tid * per), hi = min(n, lo + per);
     int run = 0, flag = 0;
+    int seg = lo / L, pos = lo - seg * L;             // position inside the segment, tracked
     for (int i = lo; i < hi; ++i) {
-        if (i % L == 0) {
+        if (pos == 0) {
             run = 0;
             flag = 1;
         }
         const int v = a[i];
         a[i] = run;
         run += v;
-        if (i % L == L - 1 && seg_total) seg_total[i / L] = v;   // keep the last value
+        if (pos == L - 1) {
+            if (seg_total) seg_total[seg] = v;       // keep the last value
+            pos = 0;
+            ++seg;
+        } else {
+            ++pos;
+        }
     }
     // inclusive segmented scan over the lanes of this wavefront
     int f = flag, v = run;
@@ -149,8 +156,9 @@ __device__ void seg_exclusive_scan(int *a, int n, int L, int *seg_total, int *wf
     int prev = __shfl_up(v, 1, 64);      // exclusive carry into this chunk
     if (lane == 0) prev = cv;
     (void)cf;
-    for (int i = lo; i < hi; ++i) {
-        if (i % L == 0) break;
+    for (int i = lo, p = lo - (lo / L) * L; i < hi; ++i, ++p) {
+        if (p == L) p = 0;
+        if (p == 0) break;
         a[i] += prev;
     }
     __syncthreads();
@@ -183,11 +191,22 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_scan(
     __syncthreads();
     for (int b = tid; b < g.B; b += kScanThreads)
         if (blk_flags[b]) atomicOr(&sflag, blk_flags[b]);
-    // block counts, transposed so that one (source, expert)'s blocks are contiguous
-    for (int i = tid; i < g.B * E; i += kScanThreads) {
-        const int b = i / E, e = i % E;
-        const int s = b / bps, bb = b % bps;
-        bct[(s * E + e) * bps + bb] = blk_counts[i];
+    // block counts, transposed so that one (source, expert)'s blocks are contiguous;
+    // thread e handles expert e (E <= kScanThreads), eight blocks' loads in flight
+    if (tid < E) {
+        for (int b0 = 0; b0 < g.B; b0 += 8) {
+            int v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = (b0 + u < g.B) ? blk_counts[size_t(b0 + u) * E + tid] : 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int b = b0 + u;
+                if (b < g.B) {
+                    const int s = b / bps, bb = b - s * bps;
+                    bct[(s * E + tid) * bps + bb] = v[u];
+                }
+            }
+        }
     }
     __syncthreads();
     // per-source counts, prefix over each source's blocks
@@ -227,12 +246,15 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_scan(
     for (int e = tid; e <= E; e += kScanThreads) expert_off[e] = tot[e];
     __syncthreads();
     if (tid == 0) *flag = sflag;      // overwrites the previous call's flag
-    // first row of every (block, expert)
-    for (int i = tid; i < g.B * E; i += kScanThreads) {
-        const int b = i / E, e = i % E;
-        const int s = b / bps, bb = b % bps, r = e / epr;
-        blk_base[i] = int(int64_t(r) * g.cap) + chk[r * (ns + 1) + s] + cnt[s * E + e] +
-                      bct[(s * E + e) * bps + bb];
+    // first row of every (block, expert): thread e handles expert e
+    if (tid < E) {
+        const int r = tid / epr;
+        const int rbase = int(int64_t(r) * g.cap);
+        for (int b = 0; b < g.B; ++b) {
+            const int s = b / bps, bb = b - s * bps;
+            blk_base[size_t(b) * E + tid] = rbase + chk[r * (ns + 1) + s] + cnt[s * E + tid] +
+                                            bct[(s * E + tid) * bps + bb];
+        }
     }
 }
 
