@@ -195,7 +195,8 @@ moe_status_t moe_expert_ffn(const void *x_disp, const int32_t *expert_off, const
  * tensor, accumulating at the receiver ([EFA] Dispatch/combine latency).
  *   y[t,:] = sum_{j<k} topk_w[t,j] * y_disp[pair_slot[t,j], :]
  * float32 accumulation in j order, one rounding to dtype. rows_total bounds
- * pair_slot (entries outside [0, rows_total) contribute nothing). */
+ * pair_slot (entries outside [0, rows_total) contribute nothing; with rows_total = 0
+ * y_disp is never read). k <= 64, else MOE_ERR_UNSUPPORTED (also for combine_add). */
 moe_status_t moe_combine(const void *y_disp, const int32_t *pair_slot, const float *topk_w,
                          int64_t T, int32_t k, int64_t d, int64_t rows_total, moe_dtype_t dtype,
                          void *y, void *stream);

@@ -105,6 +105,7 @@ def test_ffn_combine_bwd_host_validation(lib):
     assert c(FAKE, FAKE, FAKE, 10, 2, 60, 20, BF16, FAKE, None) == ALIGN
     assert c(FAKE, FAKE, FAKE, 10, 0, 64, 20, BF16, FAKE, None) == INVALID
     assert c(None, None, None, 0, 2, 64, 0, BF16, None, None) == OK
+    assert c(FAKE, FAKE, FAKE, 10, 65, 64, 20, BF16, FAKE, None) == UNSUPPORTED   # k > 64
     cb = lib.moe_combine_bwd
     assert cb(FAKE, FAKE, FAKE, FAKE, 10, 40, 64, 20, BF16, FAKE, FAKE, None) == UNSUPPORTED
     db = lib.moe_dispatch_bwd

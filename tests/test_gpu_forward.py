@@ -312,3 +312,26 @@ def test_dispatch_ep_layout_multiblock(gpu_lib, n_src, n_dst, Ts, E, k):
     rp = out["row_pair"]
     live = torch.nonzero(rp >= 0).squeeze(1)
     assert torch.equal(out["x_disp"][live].view(torch.int16), x[(rp[live] // k).long()].view(torch.int16))
+
+
+@pytest.mark.parametrize("k", [1, 6, 9, 32])
+def test_combine_gather_edges(gpu_lib, k):
+    """Combine on its own: k across the eight-row load batches, pairs whose slot is
+    negative or past rows_total (they contribute nothing, by the ABI), a ragged row
+    width; against the oracle's weighted sum over the valid pairs."""
+    moe = gpu_lib
+    T, d, rows = 300, 264, 700
+    _say(f"combine edges k={k}")
+    g = torch.Generator().manual_seed(100 + k)
+    y_disp = torch.randn(rows, d, generator=g).to(torch.bfloat16)
+    slot = torch.randint(0, rows, (T, k), generator=g, dtype=torch.int32)
+    slot[::7, 0] = -1
+    slot[::11, k - 1] = rows + 5
+    w = torch.rand(T, k, generator=g)
+    y = moe.moe_combine(y_disp.cuda(), slot.cuda(), w.cuda())
+    torch.cuda.synchronize()
+    valid = ((slot >= 0) & (slot < rows)).numpy()
+    ref = oracle.combine(y_disp, np.where(valid, slot.numpy(), 0), w.numpy() * valid)
+    err = oracle.normwise_rel_err(_np(y), ref)
+    _say(f"  err {err:.2e}")
+    assert err <= BF16_TOL

@@ -7,8 +7,8 @@
 // accumulation happens at the receiver only (Dispatch/combine latency).
 //
 // One wavefront per token; lane c owns 16-byte column chunks c, c+64, ...; the k
-// gathered rows are independent 16-byte loads (kept in flight together), summed in
-// float32 in j order and rounded once. The backward is the transpose: a scatter of
+// gathered rows are independent 16-byte loads (eight in flight together), summed in
+// float32 in j order and rounded once; lane j holds pair j's slot and gate. The backward is the transpose: a scatter of
 // w*dy into the k rows, and a dot product per (t, j) for the gate gradient.
 #include "common.h"
 
@@ -27,8 +27,9 @@ __global__ __launch_bounds__(256) void k_combine(const uint4 *__restrict__ y_dis
     const int wave0 = __builtin_amdgcn_readfirstlane((blockIdx.x * blockDim.x + threadIdx.x) / kWave);
     const int nwaves = gridDim.x * blockDim.x / kWave;
     for (int t = wave0; t < T; t += nwaves) {
-        const int *ps = pair_slot + size_t(t) * k;
-        const float *pw = topk_w + size_t(t) * k;
+        // lane j < k holds pair j's slot and gate; the row loop reads them by lane
+        const int my_s = lane < k ? pair_slot[size_t(t) * k + lane] : -1;
+        const float my_g = lane < k ? topk_w[size_t(t) * k + lane] : 0.0f;
         for (int c = lane; c < rc; c += kWave) {
             float acc[VN];
             if (residual) {
@@ -37,14 +38,27 @@ __global__ __launch_bounds__(256) void k_combine(const uint4 *__restrict__ y_dis
 #pragma unroll
                 for (int i = 0; i < VN; ++i) acc[i] = 0.0f;
             }
-            for (int j = 0; j < k; ++j) {
-                const int s = ps[j];
-                if (s < 0 || s >= rows_total) continue;
-                const float g = pw[j];
-                float f[VN];
-                Vec<DT>::unpack(y_disp[size_t(s) * rc + c], f);
+            // eight rows' loads in flight together, then their terms in j order
+            for (int j0 = 0; j0 < k; j0 += 8) {
+                uint4 v[8];
+                bool ok[8];
 #pragma unroll
-                for (int i = 0; i < VN; ++i) acc[i] = __builtin_fmaf(g, f[i], acc[i]);
+                for (int u = 0; u < 8; ++u) {
+                    const int sj = __builtin_amdgcn_readlane(my_s, min(j0 + u, kWave - 1));
+                    ok[u] = j0 + u < k && sj >= 0 && sj < rows_total;   // uniform
+                    v[u] = make_uint4(0u, 0u, 0u, 0u);
+                    if (ok[u]) v[u] = y_disp[size_t(sj) * rc + c];
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    if (!ok[u]) continue;
+                    const float g = __builtin_bit_cast(
+                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_g), j0 + u));
+                    float f[VN];
+                    Vec<DT>::unpack(v[u], f);
+#pragma unroll
+                    for (int i = 0; i < VN; ++i) acc[i] = __builtin_fmaf(g, f[i], acc[i]);
+                }
             }
             y[size_t(t) * rc + c] = Vec<DT>::pack(acc);
         }
@@ -193,7 +207,7 @@ moe_status_t combine_impl(const void *y_disp, const int32_t *pair_slot, const fl
                           const void *residual, void *y, void *stream) {
     if (!valid_dtype(dtype) || T < 0 || d <= 0 || k <= 0 || rows_total < 0)
         return MOE_ERR_INVALID_ARG;
-    if (T > (int64_t(1) << 31) / 64) return MOE_ERR_UNSUPPORTED;
+    if (T > (int64_t(1) << 31) / 64 || k > kWave) return MOE_ERR_UNSUPPORTED;
     if (T == 0) return MOE_OK;
     if (!y_disp || !pair_slot || !topk_w || !y) return MOE_ERR_INVALID_ARG;
     const int64_t rowb = d * elt_size(dtype);
