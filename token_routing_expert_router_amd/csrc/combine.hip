@@ -180,14 +180,29 @@ __global__ __launch_bounds__(256) void k_combine_partials(const uint4 *__restric
             float acc[VN];
 #pragma unroll
             for (int i = 0; i < VN; ++i) acc[i] = 0.0f;
+            // destinations ascending, four partial rows' loads in flight together
             uint64_t dm = dm0;
             while (dm) {
-                const int r = __builtin_ctzll(dm);
-                dm &= dm - 1;
-                float f[VN];
-                Vec<DT>::unpack(partial[(size_t(r) * T + t) * rc + c], f);
+                uint4 v[4];
+                bool use[4];
 #pragma unroll
-                for (int i = 0; i < VN; ++i) acc[i] += f[i];
+                for (int u = 0; u < 4; ++u) {
+                    use[u] = dm != 0;
+                    v[u] = make_uint4(0u, 0u, 0u, 0u);
+                    if (use[u]) {
+                        const int r = __builtin_ctzll(dm);
+                        dm &= dm - 1;
+                        v[u] = partial[(size_t(r) * T + t) * rc + c];
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    if (!use[u]) continue;
+                    float f[VN];
+                    Vec<DT>::unpack(v[u], f);
+#pragma unroll
+                    for (int i = 0; i < VN; ++i) acc[i] += f[i];
+                }
             }
             y[size_t(t) * rc + c] = Vec<DT>::pack(acc);
         }
