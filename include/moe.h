@@ -296,7 +296,7 @@ moe_status_t moe_combine_partials(const void *partial, const int32_t *pair_slot,
  * moe_dispatch_bwd: dx[t] = sum_j dx_disp[pair_slot[t,j]]
  *                           + sum_j dlogits_sel[t,j] * w_router[topk_idx[t,j]]
  *                   (second term skipped if dlogits_sel is NULL), float32 sum in
- *                   j order, one rounding to dtype.
+ *                   j order, one rounding to dtype; k <= 64.
  * Shapes as in the forward calls; dw13 [E,2F,d], dw2 [E,d,F], dw_router [E,d]. */
 moe_status_t moe_combine_bwd(const void *dy, const void *y_disp, const int32_t *pair_slot,
                              const float *topk_w, int64_t T, int32_t k, int64_t d,

@@ -110,6 +110,7 @@ def test_ffn_combine_bwd_host_validation(lib):
     assert cb(FAKE, FAKE, FAKE, FAKE, 10, 40, 64, 20, BF16, FAKE, FAKE, None) == UNSUPPORTED
     db = lib.moe_dispatch_bwd
     assert db(FAKE, FAKE, None, FAKE, None, 10, 2, 64, 8, 20, BF16, FAKE, None) == INVALID
+    assert db(FAKE, FAKE, None, None, None, 10, 65, 64, 8, 20, BF16, FAKE, None) == UNSUPPORTED
 
 
 def test_ep_recv_host_validation(lib):

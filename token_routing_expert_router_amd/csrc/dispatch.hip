@@ -474,28 +474,55 @@ __global__ __launch_bounds__(256) void k_dispatch_bwd(const uint4 *__restrict__ 
     const int wave0 = __builtin_amdgcn_readfirstlane((blockIdx.x * blockDim.x + threadIdx.x) / kWave);
     const int nwaves = gridDim.x * blockDim.x / kWave;
     for (int t = wave0; t < T; t += nwaves) {
-        const int *ps = pair_slot + size_t(t) * k;
+        // lane j < k holds pair j's slot, expert and router-gradient weight
+        const int my_s = lane < k ? pair_slot[size_t(t) * k + lane] : -1;
+        const int my_e = (lane < k && dl != nullptr) ? topk_idx[size_t(t) * k + lane] : -1;
+        const float my_g = (lane < k && dl != nullptr) ? dl[size_t(t) * k + lane] : 0.0f;
         for (int c = lane; c < rc; c += kWave) {
             float acc[VN];
 #pragma unroll
             for (int i = 0; i < VN; ++i) acc[i] = 0.0f;
-            for (int j = 0; j < k; ++j) {
-                const int s = ps[j];
-                if (s < 0 || s >= rows_total) continue;
-                float f[VN];
-                Vec<DT>::unpack(dx_disp[size_t(s) * rc + c], f);
+            // the k gathered rows, eight loads in flight, summed in j order
+            for (int j0 = 0; j0 < k; j0 += 8) {
+                uint4 v[8];
+                bool ok[8];
 #pragma unroll
-                for (int i = 0; i < VN; ++i) acc[i] += f[i];
+                for (int u = 0; u < 8; ++u) {
+                    const int sj = __builtin_amdgcn_readlane(my_s, min(j0 + u, kWave - 1));
+                    ok[u] = j0 + u < k && sj >= 0 && sj < rows_total;   // uniform
+                    v[u] = make_uint4(0u, 0u, 0u, 0u);
+                    if (ok[u]) v[u] = dx_disp[size_t(sj) * rc + c];
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    if (!ok[u]) continue;
+                    float f[VN];
+                    Vec<DT>::unpack(v[u], f);
+#pragma unroll
+                    for (int i = 0; i < VN; ++i) acc[i] += f[i];
+                }
             }
             if (dl != nullptr) {
-                for (int j = 0; j < k; ++j) {
-                    const int e = topk_idx[size_t(t) * k + j];
-                    if (e < 0 || e >= E) continue;
-                    const float g = dl[size_t(t) * k + j];
-                    float f[VN];
-                    Vec<DT>::unpack(w_router[size_t(e) * rc + c], f);
+                for (int j0 = 0; j0 < k; j0 += 8) {
+                    uint4 v[8];
+                    bool ok[8];
 #pragma unroll
-                    for (int i = 0; i < VN; ++i) acc[i] = __builtin_fmaf(g, f[i], acc[i]);
+                    for (int u = 0; u < 8; ++u) {
+                        const int ej = __builtin_amdgcn_readlane(my_e, min(j0 + u, kWave - 1));
+                        ok[u] = j0 + u < k && ej >= 0 && ej < E;
+                        v[u] = make_uint4(0u, 0u, 0u, 0u);
+                        if (ok[u]) v[u] = w_router[size_t(ej) * rc + c];
+                    }
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        if (!ok[u]) continue;
+                        const float g = __builtin_bit_cast(
+                            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_g), j0 + u));
+                        float f[VN];
+                        Vec<DT>::unpack(v[u], f);
+#pragma unroll
+                        for (int i = 0; i < VN; ++i) acc[i] = __builtin_fmaf(g, f[i], acc[i]);
+                    }
                 }
             }
             dx[size_t(t) * rc + c] = Vec<DT>::pack(acc);
@@ -637,6 +664,7 @@ extern "C" moe_status_t moe_dispatch_bwd(const void *dx_disp, const int32_t *pai
                                          void *dx, void *stream) {
     if (!valid_dtype(dtype) || T < 0 || d <= 0 || k <= 0 || rows_total < 0)
         return MOE_ERR_INVALID_ARG;
+    if (k > kWave) return MOE_ERR_UNSUPPORTED;
     if (T == 0) return MOE_OK;
     if (!dx_disp || !pair_slot || !dx) return MOE_ERR_INVALID_ARG;
     if (dlogits_sel && (!topk_idx || !w_router || E <= 0)) return MOE_ERR_INVALID_ARG;
