@@ -44,6 +44,8 @@ ROUTE_CASES = [
     ("mid_bf16", dict(T=100, d=8, E=16, k=2)),       # one 16-byte piece per row
     ("mid_bf16", dict(T=100, d=264, E=65, k=4)),     # just past one 64-expert group
     ("mid_bf16", dict(T=37, d=520, E=128, k=8)),     # d % 128 != 0, two expert groups
+    ("mid_bf16", dict(T=70, d=1032, E=200, k=8)),    # four expert groups, ragged T and d
+    ("mid_bf16", dict(T=50, d=256, E=449, k=8)),     # eight expert groups, 63 padded experts
     ("mid_bf16", {}),                                # the full T=4096 router, logits too
 ]
 
@@ -64,9 +66,10 @@ def test_route_parity(gpu_lib, name, kw):
     assert oracle.normwise_rel_err(_np(gates), ref_g) <= F32_TOL
 
 
-def test_route_full_softmax_flag(gpu_lib):
+@pytest.mark.parametrize("E,k", [(64, 6), (300, 8)])
+def test_route_full_softmax_flag(gpu_lib, E, k):
     moe = gpu_lib
-    wl = _wl("mid_bf16", T=300, E=64, k=6)
+    wl = _wl("mid_bf16", T=300, E=E, k=k)
     inp = moe_synth.layer_inputs(wl, with_experts=False)
     idx, gates, _ = moe.moe_route(inp["x"].cuda(), inp["w_router"].cuda(), wl.k, flags=1)
     torch.cuda.synchronize()

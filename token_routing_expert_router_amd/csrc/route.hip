@@ -12,8 +12,10 @@
 // v_mfma_f32_4x4x1_16b_f32 (sixteen 4x4 blocks, one product per output) rounds
 // exactly as fmaf(a, b, C) does. Chaining those steps over i = 0..d-1 gives the
 // canonical logits bit for bit, with the multiply-adds on the matrix cores at twice
-// the vector-ALU rate; a chain advances one step per MFMA latency, so many
-// independent 16-token x 16-expert chains are kept in flight.
+// the vector-ALU rate. Up to 64 experts, 16-token x 16-expert chains on the 4x4x1
+// form, four per workgroup (one per SIMD); above 64, 16-token x 64-expert chains on
+// v_mfma_f32_16x16x1_4b_f32 (the same single-rounding step, four times the products
+// per operand byte), 32 tokens per workgroup.
 // float32 path (vector ALU): products are not exact there, so the chains run as
 // v_fma_f32 in an LDS-tiled register-blocked kernel: a workgroup owns TT tokens and all
 // (padded) experts, each thread TM tokens x TE experts.
@@ -429,16 +431,221 @@ moe_status_t launch_route_mfma_cfg(const uint16_t *x, const uint16_t *w, int T, 
     return launch_status();
 }
 
+// ---------------------------------------------------------------- 16x16x1 chains
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Workgroup: TT = 16*TG tokens x EP = 64*EG padded experts, TG*EG chains of 16
+// tokens x 64 experts on v_mfma_f32_16x16x1_4b_f32 (four 16x16 blocks). Lane l
+// supplies row l & 15 of block l >> 4 of both operands: operand A is token l & 15 of
+// the chain's token group (the same 16 tokens in every block), operand B expert l of
+// its 64. Result register r of lane l is token 4*(l >> 4) + (r & 3), expert
+// 16*(r >> 2) + (l & 15). Waves 0..NMW-1 compute, NC chains each (one token group,
+// so operand A is read once per step for all of them); the other waves stage: raw
+// bf16 rows of the next four stages in flight in their registers, widened into the
+// float32 LDS stage. The two roles run separate loops with the same barriers, so
+// neither holds the other's registers. Padding, zero tail and the chain order are
+// those of the 4x4x1 kernel above.
+template <int TG, int EG, int NC, int BK, int NLW>
+__global__ __launch_bounds__(512) void k_router_mfma16(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, int T, int d, int E, int k,
+    int full_softmax, float *__restrict__ logits, int *__restrict__ topk_idx,
+    float *__restrict__ topk_w) {
+    constexpr int TT = 16 * TG, EP = 64 * EG;
+    constexpr int XP = BK + 4;                        // LDS row pitch (floats)
+    constexpr int CPR = BK / 8;                       // 16-byte chunks per row and stage
+    constexpr int PF = 4;                             // stages of raw rows in flight
+    constexpr int NL = 1 + NLW;                       // loads per staging thread and stage
+    constexpr int NMW = TG * EG / NC;                 // computing waves
+    constexpr int STAGE = (TT + EP) * XP;
+    constexpr int SL = EP + 1;                        // logits tile row pitch
+    static_assert(EG % NC == 0, "the chains of a wave share one token group");
+    extern __shared__ __align__(16) float smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int nthreads = int(blockDim.x);
+    const int t0 = blockIdx.x * TT;
+    // stages rounded up to a multiple of PF (the extra ones are zeros: no-op steps)
+    const int nst = (d + BK * PF - 1) / (BK * PF) * PF;
+    float *lg = smem;
+
+    if (wave >= NMW) {
+        // ---- staging: chunk = 8 elements of one row; load 0 of staging thread i is
+        // token chunk i % (TT*CPR) (stored by i < TT*CPR), loads 1.. expert chunks
+        // i + j*nstage (the host makes EP*CPR == NLW*nstage)
+        const int sti = tid - NMW * kWave;
+        const int nstage = nthreads - NMW * kWave;
+        const int xc = sti % (TT * CPR);
+        const bool xown = sti < TT * CPR;
+        const int64_t xrem = (int64_t(T) - t0) * d * 2;
+        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(x + size_t(t0) * d), 0, int(xrem < 0x7fffffff ? xrem : 0x7fffffff), 0x00020000);
+        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(w), 0, int(int64_t(E) * d * 2), 0x00020000);
+        uint32_t voff[NL];
+        int lofs[NL], coff[NL];
+        {
+            const int r = xc / CPR;
+            coff[0] = 8 * (xc % CPR);
+            voff[0] = uint32_t((min(t0 + r, T - 1) - t0) * d + coff[0]) * 2u;
+            lofs[0] = r * XP + coff[0];
+        }
+#pragma unroll
+        for (int j = 0; j < NLW; ++j) {
+            const int c = sti + j * nstage;
+            const int r = c / CPR;
+            coff[1 + j] = 8 * (c % CPR);
+            voff[1 + j] = uint32_t(min(r, E - 1) * d + coff[1 + j]) * 2u;
+            lofs[1 + j] = (TT + r) * XP + coff[1 + j];
+        }
+        uint4 raw[PF][NL];
+        auto fetch = [&](int sidx, uint4 (&dst)[NL]) {
+            const int so = sidx * BK * 2;
+            dst[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff[0], so, 0));
+#pragma unroll
+            for (int j = 1; j < NL; ++j)
+                dst[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, voff[j], so, 0));
+        };
+        auto cvt_store = [&](float *buf, int lo, uint4 u) {
+            float4 *dst = reinterpret_cast<float4 *>(buf + lo);
+            dst[0] = make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
+            dst[1] = make_float4(bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w));
+        };
+        auto stage = [&](int sidx, const uint4 (&v)[NL], float *buf) {
+            const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+            if ((sidx + 1) * BK <= d) {
+                if (xown) cvt_store(buf, lofs[0], v[0]);
+#pragma unroll
+                for (int j = 1; j < NL; ++j) cvt_store(buf, lofs[j], v[j]);
+            } else {
+                if (xown) cvt_store(buf, lofs[0], sidx * BK + coff[0] < d ? v[0] : z);
+#pragma unroll
+                for (int j = 1; j < NL; ++j) cvt_store(buf, lofs[j], sidx * BK + coff[j] < d ? v[j] : z);
+            }
+        };
+#pragma unroll
+        for (int p = 0; p < PF; ++p) fetch(p, raw[p]);
+        stage(0, raw[0], smem);
+        fetch(PF, raw[0]);
+        __syncthreads();
+        for (int s0 = 0; s0 < nst; s0 += PF) {
+#pragma unroll
+            for (int u = 0; u < PF; ++u) {
+                const int s = s0 + u;
+                stage(s + 1, raw[(u + 1) % PF], smem + ((s + 1) & 1) * STAGE);
+                __builtin_amdgcn_sched_barrier(0);
+                fetch(s + 1 + PF, raw[(u + 1) % PF]);
+                __builtin_amdgcn_sched_barrier(0);
+                __syncthreads();
+            }
+        }
+    } else {
+        // ---- chains
+        const int tg = wave / (EG / NC);
+        const int eg0 = (wave % (EG / NC)) * NC;
+        const int arow = 16 * tg + (lane & 15);
+        int brow[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) brow[c] = TT + 64 * (eg0 + c) + lane;
+        f32x16 acc[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
+        __syncthreads();
+        for (int s0 = 0; s0 < nst; s0 += PF) {
+#pragma unroll
+            for (int u = 0; u < PF; ++u) {
+                const float *cur = smem + ((s0 + u) & 1) * STAGE;
+                // operands of group g (4 steps) are read RA groups ahead of its MFMAs
+                constexpr int NG = BK / 4, RA = NG < 4 ? NG : 4;
+                f32x4 a[RA], b[RA][NC];
+                auto rd = [&](int g, f32x4 &ar, f32x4 (&br)[NC]) {
+                    ar = *reinterpret_cast<const f32x4 *>(cur + arow * XP + 4 * g);
+#pragma unroll
+                    for (int c = 0; c < NC; ++c) br[c] = *reinterpret_cast<const f32x4 *>(cur + brow[c] * XP + 4 * g);
+                };
+#pragma unroll
+                for (int g = 0; g < RA; ++g) rd(g, a[g], b[g]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    const f32x4 ag = a[g % RA];
+                    f32x4 bg[NC];
+#pragma unroll
+                    for (int c = 0; c < NC; ++c) bg[c] = b[g % RA][c];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+#pragma unroll
+                        for (int c = 0; c < NC; ++c)
+                            acc[c] = __builtin_amdgcn_mfma_f32_16x16x1f32(ag[q], bg[c][q], acc[c], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (g + RA < NG) rd(g + RA, a[g % RA], b[g % RA]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                __syncthreads();
+            }
+        }
+        // logits tile -> LDS (the staging area is free after the last barrier)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                lg[(16 * tg + 4 * (lane >> 4) + (r & 3)) * SL + 64 * (eg0 + c) + 16 * (r >> 2) + (lane & 15)] =
+                    acc[c][r];
+    }
+    __syncthreads();
+
+    if (logits != nullptr) {
+        for (int c = tid; c < TT * E; c += nthreads) {
+            const int r = c / E, e = c % E;
+            if (t0 + r < T) logits[size_t(t0 + r) * E + e] = lg[r * SL + e];
+        }
+    }
+    topk_rows<EG>(lg, SL, TT, t0, T, E, k, full_softmax, topk_idx, topk_w, wave, lane,
+                  nthreads / kWave);
+}
+
+template <int TG, int EG, int NC, int BK, int NLW>
+moe_status_t launch_route16_cfg(const uint16_t *x, const uint16_t *w, int T, int d, int E, int k,
+                                int full, float *logits, int *idx, float *gw, hipStream_t st,
+                                int nw) {
+    constexpr int TT = 16 * TG, EP = 64 * EG, NMW = TG * EG / NC;
+    const int nstage = kWave * (nw - NMW);
+    if (E > EP || nstage <= 0 || EP * (BK / 8) != NLW * nstage || TT * (BK / 8) > nstage)
+        return MOE_ERR_UNSUPPORTED;
+    if (int64_t(E) * d * 2 > 0x7fffffff || d > (1 << 26)) return MOE_ERR_UNSUPPORTED;
+    const size_t stage = size_t(TT + EP) * (BK + 4) * sizeof(float);
+    const size_t lds = std::max(2 * stage, size_t(TT) * (EP + 1) * sizeof(float));
+    if (lds > 160 * 1024) return MOE_ERR_UNSUPPORTED;
+    static std::once_flag once;
+    static bool lds_ok = false;
+    std::call_once(once, [] {
+        lds_ok = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_router_mfma16<TG, EG, NC, BK, NLW>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess;
+    });
+    if (!lds_ok) return MOE_ERR_HIP;
+    hipLaunchKernelGGL((k_router_mfma16<TG, EG, NC, BK, NLW>), dim3(unsigned(cdiv(T, TT))),
+                       dim3(kWave * nw), lds, st, x, w, T, d, E, k, full, logits, idx, gw);
+    return launch_status();
+}
+
 moe_status_t launch_route_mfma(const void *x, const void *w, int T, int d, int E, int k, int full,
                                float *logits, int *idx, float *gw, hipStream_t st) {
     const auto xb = static_cast<const uint16_t *>(x);
     const auto wb = static_cast<const uint16_t *>(w);
-    // one 16-expert chain per wave for small layers (the most chains in flight), four
-    // per wave (64 experts) for larger ones
-    if (E <= 64)   // four waves (64 padded experts), 128-deep stages
+    // up to 64 experts: one 16 x 16 4x4x1 chain per wave, four waves, 128-deep stages
+    // (a CU holds 16 x 64 outputs at 4096 tokens: one 16x16x1 chain would leave three
+    // SIMDs idle)
+    if (E <= 64)
         return launch_route_mfma_cfg<1, 1, 128, 4>(xb, wb, T, d, E, k, full, logits, idx, gw, st, 4);
-    return launch_route_mfma_cfg<4, 8, 16, 2>(xb, wb, T, d, E, k, full, logits, idx, gw, st,
-                                              int(cdiv(E, 64)));
+    // above: 32 tokens x an even number of 64-expert groups, four computing waves of
+    // EG/2 chains and four staging waves, 32-deep stages
+    const int eg = int(cdiv(E, 64));
+    if (eg <= 2) return launch_route16_cfg<2, 2, 1, 32, 2>(xb, wb, T, d, E, k, full, logits, idx, gw, st, 8);
+    if (eg <= 4) return launch_route16_cfg<2, 4, 2, 32, 4>(xb, wb, T, d, E, k, full, logits, idx, gw, st, 8);
+    if (eg <= 6) return launch_route16_cfg<2, 6, 3, 32, 6>(xb, wb, T, d, E, k, full, logits, idx, gw, st, 8);
+    return launch_route16_cfg<2, 8, 4, 32, 8>(xb, wb, T, d, E, k, full, logits, idx, gw, st, 8);
 }
 
 template <int DT, int TM>
