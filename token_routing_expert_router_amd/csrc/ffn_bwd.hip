@@ -15,6 +15,10 @@
 // pieces read by lanes a, a+4, a+8, a+12. Reductions over rows run in one fixed order
 // per output (stages in row order, MFMA k order inside), so results are bitwise
 // reproducible.
+// Waves 0-3 move every stage (each the share of two waves); waves 4-7 carry all of the
+// epilogue's global traffic. The tile leaves through LDS as whole 1 KiB rows, and only
+// the loading waves ever wait for their vector-memory counter. So the storing waves'
+// writes drain while the next item's stages load, instead of delaying its first stage.
 #include "gemm_common.h"
 
 namespace moe {
@@ -23,6 +27,7 @@ namespace {
 enum { G1_DA = 0, G2_DX = 1, G3_DW2 = 2, G4_DW13 = 3 };
 
 constexpr int kBwdThreads = 512;     // 8 waves: 4 A groups (64 rows) x 2 B groups (128 rows)
+constexpr int kLoaderWaves = 4;      // waves that issue the direct loads; the others store
 
 struct BwdArgs {
     const uint16_t *x_disp, *dy_disp, *hu, *w13, *w2;
@@ -34,6 +39,8 @@ struct BwdArgs {
 };
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u32 __attribute__((ext_vector_type(2)));
+typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
 
 // Transposed tiles: 64 k rows of 512 B (256 elements); 16-byte chunk c of k row r lives
 // at chunk c ^ swzT(r), so the four k rows one transposing read touches fall on
@@ -49,6 +56,7 @@ struct Opnd {
     int64_t nbytes;
     uint32_t off[2];
     uint32_t jstep;
+    uint32_t vstep;          // from the lane's offsets for wave w to those for wave w + 1
     uint32_t kstep;          // bytes between consecutive stages
 };
 
@@ -66,6 +74,7 @@ __device__ __forceinline__ void opnd_normal(Opnd &o, const uint16_t *base, int64
         o.off[j] = uint32_t((r * ld + c * 8) * 2);
     }
     o.jstep = uint32_t(16 * ld * 2);
+    o.vstep = uint32_t(32 * ld * 2);
     o.kstep = BK * 2;
 }
 
@@ -84,6 +93,7 @@ __device__ __forceinline__ void opnd_trans(Opnd &o, const uint16_t *base, int64_
         o.off[j] = uint32_t((kr * ld + col0 + c * 8) * 2);
     }
     o.jstep = uint32_t(4 * ld * 2);
+    o.vstep = uint32_t(8 * ld * 2);
     o.kstep = uint32_t(BK * ld * 2);
 }
 
@@ -101,23 +111,37 @@ __device__ __forceinline__ void dma16(unsigned char *dst, __amdgpu_buffer_rsrc_t
                  :: "s"(m0), "v"(voff), "s"(rs), "s"(so) : "memory", "m0");
 }
 
+// A buffer resource in scalar registers: base and size pass through readfirstlane, so
+// the compiler knows them to be wave-uniform (they are) and never hands the "s" operand
+// of the direct load a vector register.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const char *base, int64_t nbytes) {
+    const uint64_t pb = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(pb));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(pb >> 32));
+    const int n = __builtin_amdgcn_readfirstlane(int(nbytes < 0x7fffffff ? nbytes : 0x7fffffff));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>((uint64_t(hi) << 32) | lo), 0, n,
+                                             0x00020000);
+}
+
 template <bool TR>
 __device__ __forceinline__ void issue_opnd(unsigned char *tile, const Opnd &o, int kt, int wave) {
     __amdgpu_buffer_rsrc_t rs;
     uint32_t soff;
     if (TR) {
         const int64_t start = int64_t(kt) * o.kstep;
-        const int64_t rem = o.nbytes - start;        // > 0: stages start inside the data
-        rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(o.base + start), 0,
-                                               int(rem < 0x7fffffff ? rem : 0x7fffffff), 0x00020000);
+        rs = uniform_rsrc(o.base + start, o.nbytes - start);   // > 0: stages start inside the data
         soff = 0;
     } else {
-        rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(o.base), 0, int(o.nbytes), 0x00020000);
+        rs = uniform_rsrc(o.base, o.nbytes);
         soff = uint32_t(kt) * o.kstep;
     }
+    // loader wave w moves the share of waves 2w and 2w + 1 (its offsets are those of 2w)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        dma16(tile + (wave * 4 + j) * 1024, rs, o.off[j & 1], soff + uint32_t(j >> 1) * o.jstep);
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            dma16(tile + ((2 * wave + v) * 4 + j) * 1024, rs, o.off[j & 1] + uint32_t(v) * o.vstep,
+                  soff + uint32_t(j >> 1) * o.jstep);
 }
 
 // MFMA fragment (32 rows from row0, k16 step ks) of a normal tile
@@ -178,12 +202,12 @@ __device__ __forceinline__ BwdItem make_bwd_item(const BwdArgs &A, int item, con
         it.KT = K / BK;
         // B: the tile's token rows of dO (G1) or dHU (G2); rows past m_end read zeros
         const uint16_t *tb = (KIND == G1_DA) ? A.dy_disp : A.dhu;
-        opnd_normal(it.b, tb + it.m0 * K, (it.m_end - it.m0) * K * 2, K, wave, lane);
+        opnd_normal(it.b, tb + it.m0 * K, (it.m_end - it.m0) * K * 2, K, 2 * wave, lane);
         // A: W2_e [d][F] (G1) or W13_e [2F][d] (G2), k rows along the contraction
         if (KIND == G1_DA)
-            opnd_trans(it.a, A.w2 + size_t(it.e) * d * F, int64_t(d) * F * 2, F, it.a0, wave, lane);
+            opnd_trans(it.a, A.w2 + size_t(it.e) * d * F, int64_t(d) * F * 2, F, it.a0, 2 * wave, lane);
         else
-            opnd_trans(it.a, A.w13 + size_t(it.e) * F2 * d, int64_t(F2) * d * 2, d, it.a0, wave, lane);
+            opnd_trans(it.a, A.w13 + size_t(it.e) * F2 * d, int64_t(F2) * d * 2, d, it.a0, 2 * wave, lane);
     } else {
         it.e = item / (t_tiles * n_tiles);
         const int rem = item % (t_tiles * n_tiles);
@@ -194,11 +218,11 @@ __device__ __forceinline__ BwdItem make_bwd_item(const BwdArgs &A, int item, con
         it.KT = int((it.m_end - it.m0 + BK - 1) / BK);
         const int64_t nr = it.m_end - it.m0;               // rows past these read zeros
         if (KIND == G3_DW2) {        // dW2[i][f] = sum_r dO[r][i] a[r][f]
-            opnd_trans(it.a, A.act + it.m0 * F, nr * F * 2, F, it.a0, wave, lane);
-            opnd_trans(it.b, A.dy_disp + it.m0 * d, nr * d * 2, d, it.b0, wave, lane);
+            opnd_trans(it.a, A.act + it.m0 * F, nr * F * 2, F, it.a0, 2 * wave, lane);
+            opnd_trans(it.b, A.dy_disp + it.m0 * d, nr * d * 2, d, it.b0, 2 * wave, lane);
         } else {                     // dW13[j][i] = sum_r dHU[r][j] X[r][i]
-            opnd_trans(it.a, A.x_disp + it.m0 * d, nr * d * 2, d, it.a0, wave, lane);
-            opnd_trans(it.b, A.dhu + it.m0 * F2, nr * F2 * 2, F2, it.b0, wave, lane);
+            opnd_trans(it.a, A.x_disp + it.m0 * d, nr * d * 2, d, it.a0, 2 * wave, lane);
+            opnd_trans(it.b, A.dhu + it.m0 * F2, nr * F2 * 2, F2, it.b0, 2 * wave, lane);
         }
     }
     return it;
@@ -208,6 +232,7 @@ template <int KIND>
 __device__ __forceinline__ void issue_bwd_stage(unsigned char *buf, int kt, const BwdItem &it,
                                                 int wave) {
     constexpr bool BTR = !(KIND == G1_DA || KIND == G2_DX);
+    if (wave >= kLoaderWaves) return;
     issue_opnd<BTR>(buf, it.b, kt, wave);
     issue_opnd<true>(buf + kLdsA, it.a, kt, wave);
 }
@@ -247,14 +272,115 @@ __device__ __forceinline__ void mma_bwd_stage(const unsigned char *buf, int arow
     }
 }
 
+// A storing wave's 16 rows of an LDS chunk (rows lrow0..lrow0+15 of the chunk buffer,
+// tile rows trow0..): one row per instruction, lane j owning tile columns 4j..4j+3.
+// Chunk rows are 1 KiB of fp32 with 16-byte piece p of row r at p ^ (r & 15). Global
+// accesses are buffer operations on a resource that starts at the block's first row and
+// ends after its last live row: row rr is a scalar offset, rows past the item fall
+// outside (stores dropped, loads read zeros), and lanes past the last column skip.
+template <int KIND>
+__device__ __forceinline__ void store_rows(const unsigned char *cb, const BwdArgs &A,
+                                           const BwdItem &it, int trow0, int lrow0, int lane) {
+    const int d = A.d, F = A.F, F2 = 2 * F;
+    auto rd = [&](int rr) {
+        return *reinterpret_cast<const float4 *>(cb + (lrow0 + rr) * 1024 + ((lane ^ rr) << 4));
+    };
+    const int n = it.a0 + 4 * lane;
+    if (KIND == G3_DW2 || KIND == G4_DW13) {
+        const int nrows = (KIND == G3_DW2) ? d : F2;
+        const int ncols = (KIND == G3_DW2) ? F : d;
+        const int r0 = it.b0 + trow0;
+        const int live = max(0, min(16, nrows - r0));
+        const float *out = (KIND == G3_DW2) ? A.dw2 + size_t(it.e) * d * F : A.dw13 + size_t(it.e) * F2 * d;
+        const __amdgpu_buffer_rsrc_t rs =
+            uniform_rsrc(reinterpret_cast<const char *>(out + size_t(r0) * ncols), int64_t(live) * ncols * 4);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            float4 v[8];
+#pragma unroll
+            for (int rr = 0; rr < 8; ++rr) v[rr] = rd(8 * b + rr);
+            if (n < ncols) {
+#pragma unroll
+                for (int rr = 0; rr < 8; ++rr)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, v[rr]), rs, n * 4,
+                                                           (8 * b + rr) * ncols * 4, 0);
+            }
+        }
+    } else if (KIND == G2_DX) {
+        const int64_t r0 = it.m0 + trow0;
+        const int live = int(max<int64_t>(0, min<int64_t>(16, it.m_end - r0)));
+        const __amdgpu_buffer_rsrc_t rs =
+            uniform_rsrc(reinterpret_cast<const char *>(A.dx_disp + r0 * d), int64_t(live) * d * 2);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            float4 v[8];
+#pragma unroll
+            for (int rr = 0; rr < 8; ++rr) v[rr] = rd(8 * b + rr);
+            if (n < d) {
+#pragma unroll
+                for (int rr = 0; rr < 8; ++rr)
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        v2u32{pack_bf16x2(v[rr].x, v[rr].y), pack_bf16x2(v[rr].z, v[rr].w)}, rs, n * 2,
+                        (8 * b + rr) * d * 2, 0);
+            }
+        }
+    } else {
+        // dA -> dh = dA u s (1 + h (1 - s)) = dA u (s + silu(h) (1 - s)), du = dA silu(h),
+        // a = silu(h) u, with s = sigmoid(h) and silu(h) = h s; eight rows per batch, their
+        // h and u loaded together
+        const int64_t r0 = it.m0 + trow0;
+        const int live = int(max<int64_t>(0, min<int64_t>(16, it.m_end - r0)));
+        const __amdgpu_buffer_rsrc_t rhu =
+            uniform_rsrc(reinterpret_cast<const char *>(A.hu + r0 * F2), int64_t(live) * F2 * 2);
+        const __amdgpu_buffer_rsrc_t rdhu =
+            uniform_rsrc(reinterpret_cast<const char *>(A.dhu + r0 * F2), int64_t(live) * F2 * 2);
+        const __amdgpu_buffer_rsrc_t ract =
+            uniform_rsrc(reinterpret_cast<const char *>(A.act + r0 * F), int64_t(live) * F * 2);
+        const bool col = n < F;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            v2u32 hv[8], uv[8];
+#pragma unroll
+            for (int rr = 0; rr < 8; ++rr) {
+                hv[rr] = __builtin_amdgcn_raw_buffer_load_b64(rhu, n * 2, (8 * b + rr) * F2 * 2, 0);
+                uv[rr] = __builtin_amdgcn_raw_buffer_load_b64(rhu, (F + n) * 2, (8 * b + rr) * F2 * 2, 0);
+            }
+#pragma unroll
+            for (int rr = 0; rr < 8; ++rr) {
+                const float4 dv = rd(8 * b + rr);
+                const float da[4] = {dv.x, dv.y, dv.z, dv.w};
+                const float h[4] = {bf16_lo(hv[rr][0]), bf16_hi(hv[rr][0]), bf16_lo(hv[rr][1]), bf16_hi(hv[rr][1])};
+                const float u[4] = {bf16_lo(uv[rr][0]), bf16_hi(uv[rr][0]), bf16_lo(uv[rr][1]), bf16_hi(uv[rr][1])};
+                float dh[4], du[4], av[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-h[q]));
+                    const float hs = h[q] * sg;
+                    av[q] = hs * u[q];
+                    du[q] = da[q] * hs;
+                    dh[q] = (da[q] * u[q]) * __builtin_fmaf(hs, 1.0f - sg, sg);
+                }
+                if (col) {
+                    const int so2 = (8 * b + rr) * F2 * 2, so1 = (8 * b + rr) * F * 2;
+                    __builtin_amdgcn_raw_buffer_store_b64(v2u32{pack_bf16x2(dh[0], dh[1]), pack_bf16x2(dh[2], dh[3])},
+                                                          rdhu, n * 2, so2, 0);
+                    __builtin_amdgcn_raw_buffer_store_b64(v2u32{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])},
+                                                          rdhu, (F + n) * 2, so2, 0);
+                    __builtin_amdgcn_raw_buffer_store_b64(v2u32{pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3])},
+                                                          ract, n * 2, so1, 0);
+                }
+            }
+        }
+    }
+}
+
 // One work item seen by one wave with NW (0..4) live 32-row sub-tiles of output rows.
 template <int KIND, int NW>
 __device__ __forceinline__ void run_bwd_item(unsigned char *lds, const BwdArgs &A,
                                              const BwdItem &it, BwdItem &next, int nitem,
                                              const int *tile_off, int t_tiles, int n_tiles,
                                              int wave, int lane) {
-    constexpr bool DGRAD = (KIND == G1_DA || KIND == G2_DX);
-    const int d = A.d, F = A.F, F2 = 2 * F;
+    const bool loader = wave < kLoaderWaves;
     const int wn = wave & 3, wm = wave >> 2;
     f32x16 acc[4][2];
 #pragma unroll
@@ -266,87 +392,55 @@ __device__ __forceinline__ void run_bwd_item(unsigned char *lds, const BwdArgs &
     const int arow = wn * 64, brow = wm * 128;
 
     // stage 0 was issued before the previous item's epilogue (or before the first item)
-    __builtin_amdgcn_s_waitcnt(0);
+    if (loader) __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int kt = 0; kt < it.KT; ++kt) {
         unsigned char *cur = lds + (kt & 1) * (kLdsA + kLdsB);
         if (kt + 1 < it.KT) issue_bwd_stage<KIND>(lds + ((kt + 1) & 1) * (kLdsA + kLdsB), kt + 1, it, wave);
         if (NW > 0) mma_bwd_stage<KIND, NW>(cur, arow, brow, lane, acc);
-        __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the next stage landed
+        if (loader) __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the next stage landed
         __syncthreads();                 // everyone's loads landed, and cur is free
     }
 
-    // every wave is past its last LDS read: the next item's first stage flies during
-    // this item's epilogue
+    // every wave is past its last LDS read: the next item's first stage flies into buffer 0
+    // during this item's epilogue
     if (nitem >= 0) {
         next = make_bwd_item<KIND>(A, nitem, tile_off, t_tiles, n_tiles, wave, lane);
         if (next.KT > 0) issue_bwd_stage<KIND>(lds, 0, next, wave);
     }
 
-    // epilogue: lane holds output row b0 + brow + 32i + (lane & 31) and, for v = 4g + q,
-    // output column a0 + arow + 32s + 8g + 4 (lane >> 5) + q: four consecutive columns
-    const int nl = 4 * (lane >> 5);
+    // epilogue through stage buffer 1, 64 tile rows at a time. The accumulators of lane l
+    // are tile row brow + 32i + (l & 31) and, for v = 4g + q, tile column arow + 32s + 8g +
+    // 4 (l >> 5) + q. Chunk c = tile rows 64c..64c+63, held by the waves of half c >> 1
+    // (sub-tiles 2 (c & 1) and 2 (c & 1) + 1); chunks 2 and 3 go first, so the storing
+    // waves hold no accumulators any more when chunks 0 and 1 are stored.
+    unsigned char *cb = lds + (kLdsA + kLdsB);
 #pragma unroll
-    for (int i = 0; i < NW; ++i) {
-        if (DGRAD) {
-            const int64_t m = it.m0 + brow + i * 32 + (lane & 31);
-            if (m >= it.m_end) continue;
+    for (int cc = 0; cc < 4; ++cc) {
+        const int c = cc ^ 2;
+        if (wm == (c >> 1)) {
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
+            for (int ii = 0; ii < 2; ++ii) {
+                const int i = 2 * (c & 1) + ii;
+                if (i >= NW) continue;
+                const int rl = 32 * ii + (lane & 31);
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int n = it.a0 + arow + s * 32 + 8 * g + nl;
-                    if (KIND == G1_DA) {
-                        if (n >= F) continue;
-                        const uint2 hv = *reinterpret_cast<const uint2 *>(A.hu + m * F2 + n);
-                        const uint2 uv = *reinterpret_cast<const uint2 *>(A.hu + m * F2 + F + n);
-                        float h[4] = {bf16_lo(hv.x), bf16_hi(hv.x), bf16_lo(hv.y), bf16_hi(hv.y)};
-                        float u[4] = {bf16_lo(uv.x), bf16_hi(uv.x), bf16_lo(uv.y), bf16_hi(uv.y)};
-                        float dh[4], du[4], av[4];
+                for (int s = 0; s < 2; ++s)
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const float da = acc[i][s][4 * g + q];
-                            const float sg = 1.0f / (1.0f + __expf(-h[q]));
-                            dh[q] = da * u[q] * sg * (1.0f + h[q] * (1.0f - sg));
-                            du[q] = da * h[q] * sg;
-                            av[q] = silu_f(h[q]) * u[q];
-                        }
-                        uint2 ph, pu, pa;
-                        ph.x = pack_bf16x2(dh[0], dh[1]);
-                        ph.y = pack_bf16x2(dh[2], dh[3]);
-                        pu.x = pack_bf16x2(du[0], du[1]);
-                        pu.y = pack_bf16x2(du[2], du[3]);
-                        pa.x = pack_bf16x2(av[0], av[1]);
-                        pa.y = pack_bf16x2(av[2], av[3]);
-                        *reinterpret_cast<uint2 *>(A.dhu + m * F2 + n) = ph;
-                        *reinterpret_cast<uint2 *>(A.dhu + m * F2 + F + n) = pu;
-                        *reinterpret_cast<uint2 *>(A.act + m * F + n) = pa;
-                    } else {
-                        if (n >= d) continue;
-                        uint2 p;
-                        p.x = pack_bf16x2(acc[i][s][4 * g], acc[i][s][4 * g + 1]);
-                        p.y = pack_bf16x2(acc[i][s][4 * g + 2], acc[i][s][4 * g + 3]);
-                        *reinterpret_cast<uint2 *>(A.dx_disp + m * d + n) = p;
+                    for (int g = 0; g < 4; ++g) {
+                        const int pc = wn * 16 + 8 * s + 2 * g + (lane >> 5);
+                        *reinterpret_cast<float4 *>(cb + rl * 1024 + ((pc ^ (rl & 15)) << 4)) =
+                            make_float4(acc[i][s][4 * g], acc[i][s][4 * g + 1], acc[i][s][4 * g + 2],
+                                        acc[i][s][4 * g + 3]);
                     }
-                }
-        } else {
-            const int orow = it.b0 + brow + i * 32 + (lane & 31);
-            const int nrows = (KIND == G3_DW2) ? d : F2;
-            const int ncols = (KIND == G3_DW2) ? F : d;
-            if (orow >= nrows) continue;
-            float *out = (KIND == G3_DW2) ? A.dw2 + size_t(it.e) * d * F + size_t(orow) * F
-                                          : A.dw13 + size_t(it.e) * F2 * d + size_t(orow) * d;
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int n = it.a0 + arow + s * 32 + 8 * g + nl;
-                    if (n >= ncols) continue;
-                    *reinterpret_cast<float4 *>(out + n) =
-                        make_float4(acc[i][s][4 * g], acc[i][s][4 * g + 1], acc[i][s][4 * g + 2],
-                                    acc[i][s][4 * g + 3]);
-                }
+            }
         }
+        __syncthreads();
+        if (!loader) {
+            const int r0 = (wave - kLoaderWaves) * 16;
+            store_rows<KIND>(cb, A, it, 64 * c + r0, r0, lane);
+        }
+        __syncthreads();
     }
 }
 
