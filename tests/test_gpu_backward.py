@@ -94,3 +94,28 @@ def test_mid_bf16_train_full(gpu_lib):
     torch.cuda.synchronize()
     for key in ("dx", "dw_router", "dw13", "dw2", "dgates"):
         assert torch.equal(bwd[key], bwd2[key]), key
+
+
+@pytest.mark.parametrize("kw", [dict(T=300, d=256, E=8, k=2, F=192), dict(T=700, d=512, E=4, k=2, F=320)],
+                         ids=["F192", "F320"])
+def test_expert_bwd_writes_every_live_element(gpu_lib, kw):
+    """Outputs pre-filled with NaN and with zeros give bit-identical results: every
+    weight-gradient element and every live dx_disp row is written (tiles whose rows or
+    columns run past the matrix included), none is read before it is written."""
+    moe = gpu_lib
+    wl = moe_synth.small_workload(moe_synth.WORKLOADS["mid_bf16_train"], **kw)
+    inp, dy, fwd, bwd = _run(moe, wl)
+    rows_live = int(fwd["expert_off"][-1])
+    outs = []
+    for fill in (float("nan"), 0.0):
+        dxd = torch.full_like(bwd["dx_disp"], fill)
+        dw13 = torch.full_like(bwd["dw13"], fill)
+        dw2 = torch.full_like(bwd["dw2"], fill)
+        moe.moe_expert_ffn_bwd(fwd["x_disp"], bwd["dy_disp"], fwd["hu_save"], fwd["expert_off"],
+                               inp["w13"], inp["w2"], dx_disp=dxd, dw13=dw13, dw2=dw2)
+        torch.cuda.synchronize()
+        outs.append((dxd[:rows_live].clone(), dw13.clone(), dw2.clone()))
+    for a, b in zip(*outs):
+        assert torch.isfinite(a).all()
+        assert torch.equal(a, b)
+    assert torch.equal(outs[0][1], bwd["dw13"]) and torch.equal(outs[0][2], bwd["dw2"])
