@@ -5,12 +5,12 @@
 // to the grouped GEMM (Dispatch and combine). The expert form is not on the pages:
 // SwiGLU without biases, h = X W1^T, u = X W3^T, a = silu(h) * u, y = a W2^T.
 //
-// bf16 path (the only matrix-core path in the library): v_mfma_f32_32x32x16_bf16,
-// float32 accumulation. Workgroup tile 128 rows x 256 weight rows x 64 deep, four
-// wavefronts in a 2x2 grid, each 64 rows x 4 sub-tiles of 32 weight rows. For the
-// gate/up GEMM the 256 weight rows are 128 rows of W1 and the same 128 rows of W3,
-// so the SwiGLU epilogue pairs h and u in registers and only a is written. Tiles are
-// double-buffered in LDS with an XOR swizzle of 16-byte chunks. Rows are ragged per
+// bf16 path: v_mfma_f32_32x32x16_bf16, float32 accumulation. Workgroup tile 256 token
+// rows x 256 weight rows x 64 deep, eight wavefronts (each 128 token rows x 64 weight
+// rows). For the gate/up GEMM the 256 weight rows are 128 rows of W1 and the same 128
+// rows of W3, so the SwiGLU epilogue pairs h and u in registers and writes a (and h, u
+// when they are saved for the backward). Tiles are double-buffered in LDS with an XOR
+// swizzle of 16-byte chunks. Rows are ragged per
 // expert: a tile map (m-tiles per expert, prefix-summed on the device) lets a
 // persistent grid walk (expert, m-tile, n-tile) work items; the walk gives each XCD
 // a contiguous run of items in every round so tiles that share A rows or weight
@@ -27,11 +27,20 @@ namespace {
 
 enum { EPI_SWIGLU = 0, EPI_PLAIN = 1 };
 
+typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
+
 // Eight wavefronts, two per SIMD: wave w takes weight group w & 3 (64 weight rows)
 // and token group w >> 2 (128 token rows), so each SIMD holds one wave of each token
 // group and the MFMA work per SIMD is the same for any count of live token rows.
 constexpr int kFwdThreads = 512;
 constexpr int kLdsFwd = kLdsGemm;
+// Waves 0-3 issue every stage's direct loads (each the share of two waves) and alone
+// wait for the vector-memory counter; waves 4-7 carry the epilogue's global writes. So
+// one item's writes drain while the next item's stages load.
+constexpr int kLoaderWaves = 4;
+// The split pays where an item's writes are large next to its loads (down: 256 output
+// columns; gate/up when h and u are saved); gate/up writing a alone keeps every wave
+// loading and writing its own share (measured: the split costs it more than it saves).
 
 // silu(h) = h * sigmoid(h) with the hardware exp and reciprocal (the result is rounded
 // to bf16, far coarser than their error)
@@ -41,32 +50,38 @@ __device__ __forceinline__ float silu_fast(float h) {
 
 // Per-item state of the bf16 grouped GEMM: buffer resources of the token tile and
 // of the expert's weight panel, and per-lane byte offsets of the lane's 16-byte chunk
-// in each of its wave's 4 A groups and 4 B groups.
+// in the wave's A and B groups 0 and 1 (group j + 2 lies 16 rows further on, with the
+// same swizzle).
 struct GemmItem {
     __amdgpu_buffer_rsrc_t ra;   // token rows from the tile's first row on
     __amdgpu_buffer_rsrc_t rw;   // the expert's weight panel
-    uint32_t a_off[4], b_off[4];
-    int a_groups;                // of this wave's 4 A groups, those holding live rows
+    uint32_t a_off[2], b_off[2];
+    int a_groups;                // of this wave's A groups, those holding live rows
     int64_t m0, m_end;           // token rows [m0, m_end) are live in this tile
     int n0;                      // first output column
 };
 
-// Direct global->LDS loads of one stage: wave w moves A groups 4w..4w+3 and B groups
-// 4w..4w+3 (a group is 8 rows x 128 bytes, one 1 KiB wavefront instruction). Buffer
-// loads rather than global ones: the compiler then keeps its LDS waits exact.
+// Direct global->LDS loads of one stage (a group is 8 rows x 128 bytes, one 1 KiB
+// wavefront instruction). Split: loading wave w moves A and B groups 8w..8w+7, the
+// other waves nothing; else wave w moves groups 4w..4w+3. Buffer loads rather than
+// global ones: the compiler then keeps its LDS waits exact.
+template <bool SPLIT>
 __device__ __forceinline__ void issue_stage(unsigned char *lds, int stage, int k0,
-                                            const GemmItem &it, int wave) {
+                                            const GemmItem &it, int wave, int K) {
+    constexpr int NG = SPLIT ? 8 : 4;
+    if (SPLIT && wave >= kLoaderWaves) return;
     unsigned char *As = lds + stage * (kLdsA + kLdsB);
     unsigned char *Bs = As + kLdsA;
+    const uint32_t step = uint32_t(16 * K * 2);          // 16 rows
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NG; ++j) {
         if (j < it.a_groups)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                it.ra, (__attribute__((address_space(3))) void *)(As + (wave * 4 + j) * 1024), 16,
-                it.a_off[j], k0 * 2, 0, 0);
+                it.ra, (__attribute__((address_space(3))) void *)(As + (wave * NG + j) * 1024), 16,
+                it.a_off[j & 1] + uint32_t(j >> 1) * step, k0 * 2, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            it.rw, (__attribute__((address_space(3))) void *)(Bs + (wave * 4 + j) * 1024), 16,
-            it.b_off[j], k0 * 2, 0, 0);
+            it.rw, (__attribute__((address_space(3))) void *)(Bs + (wave * NG + j) * 1024), 16,
+            it.b_off[j & 1] + uint32_t(j >> 1) * step, k0 * 2, 0, 0);
     }
 }
 
@@ -92,7 +107,7 @@ __device__ __forceinline__ void read_frags(const unsigned char *As, const unsign
 // One work item, seen by one wave with NW (0..4) live 32-row token sub-tiles: the
 // whole K loop and the epilogue, branch-free in the inner loop. A wave with no live
 // rows still moves its share of every stage and joins every barrier.
-template <int EPI, int NW>
+template <int EPI, int NW, bool SPLIT>
 __device__ __forceinline__ void run_item(unsigned char *lds, const GemmItem &it,
                                          const GemmItem &next, bool has_next, int wave,
                                          int lane, int K, int N, uint16_t *__restrict__ out,
@@ -114,12 +129,13 @@ __device__ __forceinline__ void run_item(unsigned char *lds, const GemmItem &it,
     const int trow = wm * 128;
 
     const int KT = K / BK;
+    const bool loader = !SPLIT || wave < kLoaderWaves;
     // stage 0 was issued before the previous item's epilogue (or before the first item)
-    __builtin_amdgcn_s_waitcnt(0);
+    if (loader) __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int kt = 0; kt < KT; ++kt) {
         const int cur = kt & 1;
-        if (kt + 1 < KT) issue_stage(lds, cur ^ 1, (kt + 1) * BK, it, wave);
+        if (kt + 1 < KT) issue_stage<SPLIT>(lds, cur ^ 1, (kt + 1) * BK, it, wave, K);
         if (NW > 0) {
             const unsigned char *As = lds + cur * (kLdsA + kLdsB);
             const unsigned char *Bs = As + kLdsA;
@@ -144,15 +160,16 @@ __device__ __forceinline__ void run_item(unsigned char *lds, const GemmItem &it,
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the next stage landed
+        if (loader) __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the next stage landed
         __syncthreads();                 // everyone's loads landed, and cur is free
     }
 
-    // every wave is past its last LDS read: the next item's first stage flies during
-    // this item's epilogue
-    if (has_next) issue_stage(lds, 0, 0, next, wave);
+    // every wave is past its last LDS read: the next item's first stage flies into buffer
+    // 0 during this item's epilogue
+    if (has_next) issue_stage<SPLIT>(lds, 0, 0, next, wave, K);
 
-    // epilogue: D = W_tile * X_tile^T, so lane l holds token column m = l & 31 and, for
+    if (!SPLIT) {
+    // direct epilogue: D = W_tile * X_tile^T, so lane l holds token column m = l & 31 and, for
     // v = 4g + q, weight row n = 8g + 4*(l >> 5) + q: four consecutive outputs of one
     // token row, stored as one 8-byte write per (sub-tile, g)
     const int64_t mrow0 = it.m0 + trow + (lane & 31);
@@ -197,12 +214,105 @@ __device__ __forceinline__ void run_item(unsigned char *lds, const GemmItem &it,
                 }
         }
     }
+    return;
+    }
+
+    // split: epilogue through stage buffer 1 (64 KiB), CR token rows at a time. D = W_tile *
+    // X_tile^T: lane l holds token row trow + 32i + (l & 31) and, for v = 4g + q, weight
+    // row 8g + 4 (l >> 5) + q of sub-tile s, four consecutive outputs of one token row
+    // that go to LDS as one 8-byte bf16 piece. A chunk row is RP bytes: gate/up a (128
+    // columns, 256 B), with h and u behind it when they are saved; down 256 columns
+    // (512 B). Its 16-byte piece p sits at p ^ (row & 15). Chunks holding the storing
+    // waves' token half go first, so those waves hold fewer accumulators while storing.
+    const bool save = (EPI == EPI_SWIGLU) && hu_save != nullptr;
+    const int RP = (EPI == EPI_SWIGLU) ? (save ? 768 : 256) : 512;
+    const int CR = (EPI == EPI_SWIGLU) ? (save ? 64 : 256) : 128;
+    const int nch = 256 / CR;
+    unsigned char *cb = lds + (kLdsA + kLdsB);
+#pragma unroll 1
+    for (int cc = 0; cc < nch; ++cc) {
+        const int c = (cc + nch / 2) % nch;
+        const int lo = c * CR;                               // first tile row of the chunk
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            const int t0 = trow + 32 * i;
+            if (t0 < lo || t0 >= lo + CR) continue;
+            const int rl = t0 - lo + (lane & 31);
+            unsigned char *row = cb + rl * RP + (lane >> 5) * 8;
+            const int sw = rl & 15;
+            if (EPI == EPI_SWIGLU) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int pc = ((wn * 4 + g) ^ sw) << 4;
+                    float a4[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) a4[q] = silu_fast(acc[i][0][4 * g + q]) * acc[i][1][4 * g + q];
+                    *reinterpret_cast<uint2 *>(row + pc) =
+                        make_uint2(pack_bf16x2(a4[0], a4[1]), pack_bf16x2(a4[2], a4[3]));
+                    if (save) {
+                        *reinterpret_cast<uint2 *>(row + 256 + pc) =
+                            make_uint2(pack_bf16x2(acc[i][0][4 * g], acc[i][0][4 * g + 1]),
+                                       pack_bf16x2(acc[i][0][4 * g + 2], acc[i][0][4 * g + 3]));
+                        *reinterpret_cast<uint2 *>(row + 512 + pc) =
+                            make_uint2(pack_bf16x2(acc[i][1][4 * g], acc[i][1][4 * g + 1]),
+                                       pack_bf16x2(acc[i][1][4 * g + 2], acc[i][1][4 * g + 3]));
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int pc = ((wn * 8 + s2 * 4 + g) ^ sw) << 4;
+                        *reinterpret_cast<uint2 *>(row + pc) =
+                            make_uint2(pack_bf16x2(acc[i][s2][4 * g], acc[i][s2][4 * g + 1]),
+                                       pack_bf16x2(acc[i][s2][4 * g + 2], acc[i][s2][4 * g + 3]));
+                    }
+            }
+        }
+        __syncthreads();
+        if (!loader) {
+            // this wave's CR/4 rows of the chunk in whole 16-byte pieces: gate/up 16 lanes
+            // per 256-byte section row (4 rows per instruction), down 32 lanes per row (2
+            // rows per instruction); buffer stores from the wave's first token row (rows
+            // past the item and columns past N are skipped)
+            const int nr = CR / 4;
+            const int r0 = (wave - kLoaderWaves) * nr;
+            const int64_t m0 = it.m0 + lo + r0;
+            const int live = int(max<int64_t>(0, min<int64_t>(nr, it.m_end - m0)));
+            constexpr int LPR = (EPI == EPI_SWIGLU) ? 16 : 32;      // lanes per row
+            constexpr int RPI = 64 / LPR;                           // rows per instruction
+            const int pr = lane % LPR, rsub = lane / LPR;
+            const int n = it.n0 + 8 * pr;
+            const bool col = n < N;
+            const int ld = 2 * N;                                   // hu_save row length
+            const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+                out + m0 * N, 0, int(int64_t(live) * N * 2), 0x00020000);
+#pragma unroll 4
+            for (int k = 0; k < nr / RPI; ++k) {
+                const int rr = k * RPI + rsub;
+                const int rowb = (r0 + rr) * RP + ((pr ^ ((r0 + rr) & 15)) << 4);
+                if (!(col && rr < live)) continue;
+                const uint4 v = *reinterpret_cast<const uint4 *>(cb + rowb);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, v), ro, (rr * N + n) * 2, 0, 0);
+                if (save) {
+                    const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+                        hu_save + m0 * ld, 0, int(int64_t(live) * ld * 2), 0x00020000);
+                    const uint4 h = *reinterpret_cast<const uint4 *>(cb + rowb + 256);
+                    const uint4 u = *reinterpret_cast<const uint4 *>(cb + rowb + 512);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, h), rh, (rr * ld + n) * 2, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, u), rh, (rr * ld + N + n) * 2, 0, 0);
+                }
+            }
+        }
+        __syncthreads();
+    }
 }
 
 // Work item -> per-wave load state. An expert's rows are split into equal m-tiles, so
 // the tiles that share one weight panel run at one speed and meet in L2; rows past the
 // allocation are never touched, whatever expert_off holds.
-template <int EPI>
+template <int EPI, bool SPLIT>
 __device__ __forceinline__ GemmItem make_item(int item, const int *tile_off,
                                               const int *__restrict__ expert_off, int E,
                                               int n_tiles, const uint16_t *__restrict__ A,
@@ -230,27 +340,23 @@ __device__ __forceinline__ GemmItem make_item(int item, const int *tile_off,
                                              0x00020000);
     it.rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(W + size_t(e) * Nw * K), 0,
                                              int(size_t(Nw) * K * 2), 0x00020000);
-    it.a_groups = int(min<int64_t>(4, max<int64_t>(0, (it.m_end - it.m0 - wave * 32 + 7) / 8)));
+    const int wr0 = SPLIT ? (wave & 3) * 64 : wave * 32;        // the wave's first tile row
+    it.a_groups = int(min<int64_t>(SPLIT ? 8 : 4, max<int64_t>(0, (it.m_end - it.m0 - wr0 + 7) / 8)));
+    // Rows past the tile's data read zeros (outside the token resource) or stay inside
+    // the weight panel (gate rows past N read up rows) or past it (zeros): the outputs of
+    // such rows and columns are never stored. (Offsets of non-loading waves go unused.)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int g = wave * 4 + j;
-        const int r = g * 8 + lrow;              // tile row 0..255
+    for (int j = 0; j < 2; ++j) {
+        const int r = wr0 + j * 8 + lrow;               // tile row of group j
         const int c = pchunk ^ swz(r);
-        const int64_t tr = min<int64_t>(it.m0 + r, rows_alloc - 1);
-        it.a_off[j] = uint32_t(((tr - it.m0) * K + c * 8) * 2);
-        int wr;
-        if (EPI == EPI_SWIGLU) {
-            const int n = min(it.n0 + (r & 127), N - 1);
-            wr = (r < 128) ? n : N + n;
-        } else {
-            wr = min(it.n0 + r, N - 1);
-        }
+        it.a_off[j] = uint32_t((r * K + c * 8) * 2);
+        const int wr = (EPI == EPI_SWIGLU) ? it.n0 + (r & 127) + (r < 128 ? 0 : N) : it.n0 + r;
         it.b_off[j] = uint32_t((size_t(wr) * K + c * 8) * 2);
     }
     return it;
 }
 
-template <int EPI>
+template <int EPI, bool SPLIT>
 __global__ __launch_bounds__(kFwdThreads) void k_gemm_bf16(
     const uint16_t *__restrict__ A,        // token rows [rows, K]
     const int *__restrict__ expert_off,    // [E+1]
@@ -274,26 +380,26 @@ __global__ __launch_bounds__(kFwdThreads) void k_gemm_bf16(
     const int slot = (G % 8 == 0) ? (blockIdx.x % 8) * per + blockIdx.x / 8 : blockIdx.x;
     if (slot >= total) return;
 
-    GemmItem it = make_item<EPI>(slot, tile_off, expert_off, E, n_tiles, A, W, K, N, rows_alloc,
+    GemmItem it = make_item<EPI, SPLIT>(slot, tile_off, expert_off, E, n_tiles, A, W, K, N, rows_alloc,
                                  wave, lane);
-    issue_stage(lds, 0, 0, it, wave);
+    issue_stage<SPLIT>(lds, 0, 0, it, wave, K);
     for (int base = 0; base < total; base += G) {
         const int nbase = base + G;
         const int nitem = nbase + (slot + nbase / G) % G;
         const bool has_next = nitem < total;
         GemmItem next = it;
         if (has_next)
-            next = make_item<EPI>(nitem, tile_off, expert_off, E, n_tiles, A, W, K, N, rows_alloc,
+            next = make_item<EPI, SPLIT>(nitem, tile_off, expert_off, E, n_tiles, A, W, K, N, rows_alloc,
                                   wave, lane);
         // live 32-row token sub-tiles of this wave's token group
         const int nsub = int(min<int64_t>(8, (it.m_end - it.m0 + 31) / 32));
         const int nw = min(4, max(0, nsub - (wave >> 2) * 4));
         switch (nw) {
-        case 4: run_item<EPI, 4>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
-        case 3: run_item<EPI, 3>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
-        case 2: run_item<EPI, 2>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
-        case 1: run_item<EPI, 1>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
-        default: run_item<EPI, 0>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
+        case 4: run_item<EPI, 4, SPLIT>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
+        case 3: run_item<EPI, 3, SPLIT>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
+        case 2: run_item<EPI, 2, SPLIT>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
+        case 1: run_item<EPI, 1, SPLIT>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
+        default: run_item<EPI, 0, SPLIT>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
         }
         if (!has_next) break;
         it = next;
@@ -386,9 +492,11 @@ bool set_lds_limits() {
     static bool ok = false;
     static std::once_flag once;
     std::call_once(once, [] {
-        ok = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_bf16<EPI_SWIGLU>),
+        ok = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_bf16<EPI_SWIGLU, false>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, kLdsFwd) == hipSuccess &&
-             hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_bf16<EPI_PLAIN>),
+             hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_bf16<EPI_SWIGLU, true>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, kLdsFwd) == hipSuccess &&
+             hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_bf16<EPI_PLAIN, true>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, kLdsFwd) == hipSuccess;
     });
     return ok;
@@ -417,10 +525,17 @@ moe_status_t launch_gate_up(const void *x_disp, const int32_t *expert_off, const
         if (!set_lds_limits()) return MOE_ERR_HIP;
         const int nt = int(cdiv(F, BNW / 2));
         const int g = int(std::min<int64_t>((cdiv(rows, BM) + E) * nt, num_cus()));
-        hipLaunchKernelGGL(k_gemm_bf16<EPI_SWIGLU>, dim3(g), dim3(kFwdThreads), kLdsFwd, st,
-                           static_cast<const uint16_t *>(x_disp), expert_off, E,
-                           static_cast<const uint16_t *>(w13), int(d), int(F), rows,
-                           static_cast<uint16_t *>(act), static_cast<uint16_t *>(hu_save), nt);
+        // writing h and u as well: the loader/storer split
+        if (hu_save != nullptr)
+            hipLaunchKernelGGL((k_gemm_bf16<EPI_SWIGLU, true>), dim3(g), dim3(kFwdThreads), kLdsFwd, st,
+                               static_cast<const uint16_t *>(x_disp), expert_off, E,
+                               static_cast<const uint16_t *>(w13), int(d), int(F), rows,
+                               static_cast<uint16_t *>(act), static_cast<uint16_t *>(hu_save), nt);
+        else
+            hipLaunchKernelGGL((k_gemm_bf16<EPI_SWIGLU, false>), dim3(g), dim3(kFwdThreads), kLdsFwd, st,
+                               static_cast<const uint16_t *>(x_disp), expert_off, E,
+                               static_cast<const uint16_t *>(w13), int(d), int(F), rows,
+                               static_cast<uint16_t *>(act), nullptr, nt);
     } else {
         const int nt = int(cdiv(F, FT));
         const int g = int(std::min<int64_t>((cdiv(rows, FT) + E) * nt, 4 * num_cus()));
@@ -439,7 +554,7 @@ moe_status_t launch_down(const void *act, const int32_t *expert_off, const void 
         if (!set_lds_limits()) return MOE_ERR_HIP;
         const int nt = int(cdiv(d, BNW));
         const int g = int(std::min<int64_t>((cdiv(rows, BM) + E) * nt, num_cus()));
-        hipLaunchKernelGGL(k_gemm_bf16<EPI_PLAIN>, dim3(g), dim3(kFwdThreads), kLdsFwd, st,
+        hipLaunchKernelGGL((k_gemm_bf16<EPI_PLAIN, true>), dim3(g), dim3(kFwdThreads), kLdsFwd, st,
                            static_cast<const uint16_t *>(act), expert_off, E,
                            static_cast<const uint16_t *>(w2), int(F), int(d), rows,
                            static_cast<uint16_t *>(y_disp), nullptr, nt);

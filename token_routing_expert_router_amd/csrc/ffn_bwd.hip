@@ -276,8 +276,10 @@ __device__ __forceinline__ void mma_bwd_stage(const unsigned char *buf, int arow
 // tile rows trow0..): one row per instruction, lane j owning tile columns 4j..4j+3.
 // Chunk rows are 1 KiB of fp32 with 16-byte piece p of row r at p ^ (r & 15). Global
 // accesses are buffer operations on a resource that starts at the block's first row and
-// ends after its last live row: row rr is a scalar offset, rows past the item fall
-// outside (stores dropped, loads read zeros), and lanes past the last column skip.
+// ends after its last live row, with row rr as the scalar offset (on gfx950 the range
+// check covers the scalar offset too: measured, loads past the end read zeros and
+// stores are dropped). Rows past the item (rr >= live, a wave-uniform test) and lanes
+// past the last column are also skipped explicitly.
 template <int KIND>
 __device__ __forceinline__ void store_rows(const unsigned char *cb, const BwdArgs &A,
                                            const BwdItem &it, int trow0, int lrow0, int lane) {
@@ -302,8 +304,9 @@ __device__ __forceinline__ void store_rows(const unsigned char *cb, const BwdArg
             if (n < ncols) {
 #pragma unroll
                 for (int rr = 0; rr < 8; ++rr)
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, v[rr]), rs, n * 4,
-                                                           (8 * b + rr) * ncols * 4, 0);
+                    if (8 * b + rr < live)
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, v[rr]), rs, n * 4,
+                                                               (8 * b + rr) * ncols * 4, 0);
             }
         }
     } else if (KIND == G2_DX) {
@@ -319,9 +322,10 @@ __device__ __forceinline__ void store_rows(const unsigned char *cb, const BwdArg
             if (n < d) {
 #pragma unroll
                 for (int rr = 0; rr < 8; ++rr)
-                    __builtin_amdgcn_raw_buffer_store_b64(
-                        v2u32{pack_bf16x2(v[rr].x, v[rr].y), pack_bf16x2(v[rr].z, v[rr].w)}, rs, n * 2,
-                        (8 * b + rr) * d * 2, 0);
+                    if (8 * b + rr < live)
+                        __builtin_amdgcn_raw_buffer_store_b64(
+                            v2u32{pack_bf16x2(v[rr].x, v[rr].y), pack_bf16x2(v[rr].z, v[rr].w)}, rs, n * 2,
+                            (8 * b + rr) * d * 2, 0);
             }
         }
     } else {
@@ -342,8 +346,11 @@ __device__ __forceinline__ void store_rows(const unsigned char *cb, const BwdArg
             v2u32 hv[8], uv[8];
 #pragma unroll
             for (int rr = 0; rr < 8; ++rr) {
-                hv[rr] = __builtin_amdgcn_raw_buffer_load_b64(rhu, n * 2, (8 * b + rr) * F2 * 2, 0);
-                uv[rr] = __builtin_amdgcn_raw_buffer_load_b64(rhu, (F + n) * 2, (8 * b + rr) * F2 * 2, 0);
+                hv[rr] = uv[rr] = v2u32{0u, 0u};
+                if (8 * b + rr < live) {
+                    hv[rr] = __builtin_amdgcn_raw_buffer_load_b64(rhu, n * 2, (8 * b + rr) * F2 * 2, 0);
+                    uv[rr] = __builtin_amdgcn_raw_buffer_load_b64(rhu, (F + n) * 2, (8 * b + rr) * F2 * 2, 0);
+                }
             }
 #pragma unroll
             for (int rr = 0; rr < 8; ++rr) {
@@ -360,7 +367,7 @@ __device__ __forceinline__ void store_rows(const unsigned char *cb, const BwdArg
                     du[q] = da[q] * hs;
                     dh[q] = (da[q] * u[q]) * __builtin_fmaf(hs, 1.0f - sg, sg);
                 }
-                if (col) {
+                if (col && 8 * b + rr < live) {
                     const int so2 = (8 * b + rr) * F2 * 2, so1 = (8 * b + rr) * F * 2;
                     __builtin_amdgcn_raw_buffer_store_b64(v2u32{pack_bf16x2(dh[0], dh[1]), pack_bf16x2(dh[2], dh[3])},
                                                           rdhu, n * 2, so2, 0);
