@@ -55,6 +55,7 @@ BWD_CASES = [
     dict(T=77, d=128, E=16, k=3, F=64),        # ragged rows, experts with no token
     dict(T=700, d=512, E=4, k=2, F=320),       # several 256-row tiles per expert
     dict(T=64, d=192, E=64, k=6, F=128),       # most experts empty or nearly so
+    dict(T=150, d=128, E=16, k=10, F=64),      # k above 8: the multi-batch gathers
 ]
 
 

@@ -66,7 +66,10 @@ __global__ __launch_bounds__(256) void k_combine(const uint4 *__restrict__ y_dis
 }
 
 // dy_disp[pair_slot[t,j]] = w[t,j] * dy[t];  dtopk_w[t,j] = <dy[t], y_disp[pair_slot[t,j]]>
-// (one pass over the row per j; the token's dy row stays in cache between passes)
+// For k <= 8 one pass over the row serves all pairs (the dy chunk and the k gathered
+// chunks in flight together, a partial dot product per pair in registers); above that,
+// one pass per pair, the token's dy row staying in cache between passes. Both sum each
+// dot product in the same per-lane order and butterfly, so they agree bit for bit.
 template <int DT>
 __global__ __launch_bounds__(256) void k_combine_bwd(const uint4 *__restrict__ dy,
                                                      const uint4 *__restrict__ y_disp,
@@ -80,6 +83,54 @@ __global__ __launch_bounds__(256) void k_combine_bwd(const uint4 *__restrict__ d
     const int wave0 = __builtin_amdgcn_readfirstlane((blockIdx.x * blockDim.x + threadIdx.x) / kWave);
     const int nwaves = gridDim.x * blockDim.x / kWave;
     for (int t = wave0; t < T; t += nwaves) {
+        if (k <= 8) {
+            // one pass over the row for all k pairs: the dy chunk and the k gathered chunks
+            // in flight together; per pair the same per-lane order over c and the same
+            // butterfly as the pass-per-pair form below
+            const int my_s = lane < k ? pair_slot[size_t(t) * k + lane] : -1;
+            const float my_w = lane < k ? topk_w[size_t(t) * k + lane] : 0.0f;
+            float dot[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) dot[u] = 0.0f;
+            for (int c = lane; c < rc; c += kWave) {
+                const uint4 gv = dy[size_t(t) * rc + c];
+                uint4 v[8];
+                bool ok[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int su = __builtin_amdgcn_readlane(my_s, u);
+                    ok[u] = u < k && su >= 0 && su < rows_total;   // uniform
+                    v[u] = make_uint4(0u, 0u, 0u, 0u);
+                    if (ok[u]) v[u] = y_disp[size_t(su) * rc + c];
+                }
+                float g[VN];
+                Vec<DT>::unpack(gv, g);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    if (!ok[u]) continue;
+                    const int su = __builtin_amdgcn_readlane(my_s, u);
+                    const float w = __builtin_bit_cast(
+                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), u));
+                    float f[VN], o[VN];
+                    Vec<DT>::unpack(v[u], f);
+#pragma unroll
+                    for (int i = 0; i < VN; ++i) {
+                        dot[u] = __builtin_fmaf(g[i], f[i], dot[u]);
+                        o[i] = w * g[i];
+                    }
+                    dy_disp[size_t(su) * rc + c] = Vec<DT>::pack(o);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (u >= k) break;
+                float dv = dot[u];
+#pragma unroll
+                for (int off = kWave / 2; off > 0; off >>= 1) dv += __shfl_xor(dv, off, kWave);
+                if (lane == 0) dtopk_w[size_t(t) * k + u] = dv;
+            }
+            continue;
+        }
         for (int j = 0; j < k; ++j) {
             const int s = pair_slot[size_t(t) * k + j];
             const bool ok = s >= 0 && s < rows_total;
