@@ -78,6 +78,22 @@ def test_fp8_payload_crafted_rows(gpu_lib):
     _check_payload(x, plan, 1)
 
 
+@pytest.mark.parametrize("d", [128, 1024, 8192, 8320, 16512])
+def test_fp8_payload_row_widths(gpu_lib, d):
+    """Rows of one block, of exactly one and of just over one 8192-element batch of
+    the quantizing copy, and of two batches plus a block."""
+    moe = gpu_lib
+    wl = moe_synth.small_workload(moe_synth.WORKLOADS["mid_bf16"], T=40, d=d, E=8, k=3)
+    _say(f"fp8 payload width {wl}")
+    inp = moe_synth.layer_inputs(wl, device="cuda", with_experts=False)
+    idx, _, _ = moe.moe_route(inp["x"], inp["w_router"], wl.k)
+    plan = moe.moe_dispatch_fp8(inp["x"], idx, wl.E)
+    assert moe.moe_dispatch_status(plan["ws"]) == 0
+    torch.cuda.synchronize()
+    live, _ = _check_payload(inp["x"], plan, wl.k)
+    assert live.numel() == wl.T * wl.k
+
+
 @pytest.mark.parametrize("name", ["mid_bf16", "ep32_zipf"])
 def test_fp8_payload_and_dequant(gpu_lib, name):
     moe = gpu_lib

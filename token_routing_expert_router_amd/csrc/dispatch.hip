@@ -416,18 +416,45 @@ __global__ __launch_bounds__(kCopyThreads) void k_plan_slots_copy(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int tcount = min(kSubTokens, n - q * kSubTokens);
     if (Q8) {
-        // a row is rc/2 pieces of 16 elements (16 code bytes); 8 lanes hold one block
+        // a row is rc/2 pieces of 16 elements (16 code bytes); 8 lanes hold one block.
+        // Batches of 8 pieces per lane (8192 elements): all their loads in flight
+        // together, then the codes; the batch's 64 block scales are gathered so that
+        // lane L holds block L's, and each destination row gets them in one write.
         const int rp = rc / 2, nb = rc / 16;
         for (int i = wave; i < tcount; i += kCopyThreads / kWave) {
             const uint4 *src = x + size_t(t_begin + q * kSubTokens + i) * rc;
-            for (int c = lane; c < rp; c += kWave) {
-                float sc;
-                const uint4 code = quant16_fp8(src[2 * c], src[2 * c + 1], sc);
+            for (int c0 = 0; c0 < rp; c0 += 8 * kWave) {
+                uint4 v[8][2];
+#pragma unroll
+                for (int it = 0; it < 8; ++it) {
+                    const int c = c0 + it * kWave + lane;
+                    v[it][0] = make_uint4(0u, 0u, 0u, 0u);
+                    v[it][1] = make_uint4(0u, 0u, 0u, 0u);
+                    if (c < rp) {
+                        v[it][0] = src[2 * c];
+                        v[it][1] = src[2 * c + 1];
+                    }
+                }
+                uint4 code[8];
+                float my_sc = 0.0f;
+#pragma unroll
+                for (int it = 0; it < 8; ++it) {
+                    float sc;
+                    code[it] = quant16_fp8(v[it][0], v[it][1], sc);   // every lane takes part
+                    // block it*8 + (lane & 7) of the batch sits in lanes 8 (lane & 7) + 0..7
+                    const float bs = __shfl(sc, (lane & 7) * 8, kWave);
+                    if ((lane >> 3) == it) my_sc = bs;
+                }
+                const int blk = c0 / 8 + lane;                         // block held by this lane
                 for (int j = 0; j < g.k; ++j) {
                     const int sj = sl[i][j];
                     if (sj < 0 || sj >= rows_total) continue;
-                    q_disp[size_t(sj) * rp + c] = code;
-                    if ((lane & 7) == 0) q_scale[size_t(sj) * nb + c / 8] = sc;
+#pragma unroll
+                    for (int it = 0; it < 8; ++it) {
+                        const int c = c0 + it * kWave + lane;
+                        if (c < rp) q_disp[size_t(sj) * rp + c] = code[it];
+                    }
+                    if (blk < nb) q_scale[size_t(sj) * nb + blk] = my_sc;
                 }
             }
         }
