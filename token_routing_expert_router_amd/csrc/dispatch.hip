@@ -462,26 +462,24 @@ __global__ __launch_bounds__(kCopyThreads) void k_plan_slots_copy(
     }
     for (int i = wave; i < tcount; i += kCopyThreads / kWave) {
         const uint4 *src = x + size_t(t_begin + q * kSubTokens + i) * rc;
-        int c = lane;
-        for (; c + 3 * kWave < rc; c += 4 * kWave) {
-            const uint4 v0 = src[c], v1 = src[c + kWave], v2 = src[c + 2 * kWave],
-                        v3 = src[c + 3 * kWave];
+        // batches of 16 KiB of the row (16 pieces per lane) with all loads in flight
+        for (int c0 = 0; c0 < rc; c0 += 16 * kWave) {
+            uint4 v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int c = c0 + u * kWave + lane;
+                v[u] = make_uint4(0u, 0u, 0u, 0u);
+                if (c < rc) v[u] = src[c];
+            }
             for (int j = 0; j < g.k; ++j) {
                 const int sj = sl[i][j];
                 if (sj < 0 || sj >= rows_total) continue;
                 uint4 *dst = x_disp + size_t(sj) * rc;
-                dst[c] = v0;
-                dst[c + kWave] = v1;
-                dst[c + 2 * kWave] = v2;
-                dst[c + 3 * kWave] = v3;
-            }
-        }
-        for (; c < rc; c += kWave) {
-            const uint4 v = src[c];
-            for (int j = 0; j < g.k; ++j) {
-                const int sj = sl[i][j];
-                if (sj < 0 || sj >= rows_total) continue;
-                x_disp[size_t(sj) * rc + c] = v;
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    const int c = c0 + u * kWave + lane;
+                    if (c < rc) dst[c] = v[u];
+                }
             }
         }
     }
