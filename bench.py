@@ -5,8 +5,8 @@ Headline step = one forward pass of the layer over one batch of synthetic tokens
 already resident in HBM: moe_route -> moe_dispatch -> moe_expert_ffn_gate_up ->
 moe_expert_ffn_down -> moe_combine (all libmoe HIP kernels), on the T=4096, d=2048,
 E=64, k=6, F=1408 bf16 layer. The same JSON line also reports:
-  train_step   forward + backward of that layer (combine_bwd, expert_ffn_bwd,
-               route_bwd, dispatch_bwd) on the same shapes,
+  train_step   forward + backward of that layer (combine_bwd, route_bwd,
+               expert_ffn_bwd, dispatch_bwd) on the same shapes,
   ep_dispatch_combine  the rank-major dispatch and combine of 32 source ranks x 128
                tokens, d=7168, E=384, k=8, Zipf(1.2) routing (identity experts), and
                destination 0's receive path (reorder, 12-expert SwiGLU GEMM, scatter),
@@ -205,11 +205,13 @@ def train_bench(torch, moe, wl, dev, steps, warmup):
         ev[1].record()
         moe.moe_combine_bwd(dy, y_disp, plan["pair_slot"], gates, dy_disp=dy_disp, dtopk_w=dgates)
         ev[2].record()
-        moe.moe_expert_ffn_bwd(plan["x_disp"], dy_disp, hu, plan["expert_off"], w13, w2,
-                               dx_disp=dx_disp, dw13=dw13, dw2=dw2, ws=ws)
-        ev[3].record()
+        # the router's backward needs only the gate gradients; running it before the
+        # expert backward puts dx_disp's writer right before its reader
         moe.moe_route_bwd(x, idx, gates, dgates, plan["expert_off"], plan["row_pair"], E,
                           dlogits_sel=dl, dw_router=dwr)
+        ev[3].record()
+        moe.moe_expert_ffn_bwd(plan["x_disp"], dy_disp, hu, plan["expert_off"], w13, w2,
+                               dx_disp=dx_disp, dw13=dw13, dw2=dw2, ws=ws)
         ev[4].record()
         moe.moe_dispatch_bwd(dx_disp, plan["pair_slot"], topk_idx=idx, dlogits_sel=dl,
                              w_router=wr, dx=dx)
@@ -219,7 +221,7 @@ def train_bench(torch, moe, wl, dev, steps, warmup):
     fwd_work = {"forward": dict(bytes=sum(w["bytes"] for w in stage_work(wl).values()),
                                 flops=sum(w["flops"] for w in stage_work(wl).values()), unit="mfma")}
     fwd_work.update(bwd_work(wl))
-    stages = summarize(["forward", "combine_bwd", "expert_ffn_bwd", "route_bwd", "dispatch_bwd"],
+    stages = summarize(["forward", "combine_bwd", "route_bwd", "expert_ffn_bwd", "dispatch_bwd"],
                        events, steps, fwd_work)
     del inp
     return {"workload": f"{wl.name}: forward + backward, T={T} d={d} E={E} k={k} F={F} bf16, "

@@ -501,15 +501,16 @@ def forward_microbatched(x, w_router, w13, w2, k: int, n_micro: int = 2, *, stre
 # ------------------------------------------------------------ whole layer
 def backward(x, w_router, w13, w2, fwd: dict, dy, *, stream=None):
     """Gradients of sum(dy * y) for a forward() run with save_for_backward=True:
-    combine_bwd -> expert_ffn_bwd -> route_bwd -> dispatch_bwd. Returns a dict with
-    dx, dw_router, dw13, dw2 and the intermediates."""
+    combine_bwd -> route_bwd -> expert_ffn_bwd -> dispatch_bwd (the router's backward
+    needs only the gate gradients, so dx_disp is written right before it is gathered).
+    Returns a dict with dx, dw_router, dw13, dw2 and the intermediates."""
     E = w_router.shape[0]
     dy_disp, dgates = moe_combine_bwd(dy, fwd["y_disp"], fwd["pair_slot"], fwd["topk_w"],
                                       stream=stream)
-    dx_disp, dw13, dw2 = moe_expert_ffn_bwd(fwd["x_disp"], dy_disp, fwd["hu_save"],
-                                            fwd["expert_off"], w13, w2, stream=stream)
     dl, dwr = moe_route_bwd(x, fwd["topk_idx"], fwd["topk_w"], dgates, fwd["expert_off"],
                             fwd["row_pair"], E, stream=stream)
+    dx_disp, dw13, dw2 = moe_expert_ffn_bwd(fwd["x_disp"], dy_disp, fwd["hu_save"],
+                                            fwd["expert_off"], w13, w2, stream=stream)
     dx = moe_dispatch_bwd(dx_disp, fwd["pair_slot"], topk_idx=fwd["topk_idx"], dlogits_sel=dl,
                           w_router=w_router, stream=stream)
     return dict(dy_disp=dy_disp, dgates=dgates, dx_disp=dx_disp, dw13=dw13, dw2=dw2,

@@ -566,16 +566,16 @@ extern "C" moe_status_t moe_expert_ffn_bwd(const void *x_disp, const void *dy_di
         const int g = int(std::min<int64_t>(int64_t(E) * tt * nt, cus));
         hipLaunchKernelGGL(k_gemm_bwd<G3_DW2>, dim3(g), dim3(kBwdThreads), 0, st, A, tt, nt);
     }
+    {   // G4: dW13 (before G2, so dx_disp is the last thing written)
+        const int tt = int(cdiv(2 * F, BM)), nt = int(cdiv(d, BNW));
+        const int g = int(std::min<int64_t>(int64_t(E) * tt * nt, cus));
+        hipLaunchKernelGGL(k_gemm_bwd<G4_DW13>, dim3(g), dim3(kBwdThreads), 0, st, A, tt, nt);
+    }
     {   // G2: dX
         const int nt = int(cdiv(d, BNW));
         const int g = int(std::min<int64_t>(max_mt * nt, cus));
         if (g > 0)
             hipLaunchKernelGGL(k_gemm_bwd<G2_DX>, dim3(g), dim3(kBwdThreads), 0, st, A, 0, nt);
-    }
-    {   // G4: dW13
-        const int tt = int(cdiv(2 * F, BM)), nt = int(cdiv(d, BNW));
-        const int g = int(std::min<int64_t>(int64_t(E) * tt * nt, cus));
-        hipLaunchKernelGGL(k_gemm_bwd<G4_DW13>, dim3(g), dim3(kBwdThreads), 0, st, A, tt, nt);
     }
     return launch_status();
 }
