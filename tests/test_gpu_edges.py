@@ -1,4 +1,5 @@
-"""GPU parity at the limits and degenerate routings of dispatch -> expert FFN -> combine.
+"""GPU parity at the limits and degenerate routings of dispatch -> expert FFN -> combine,
+and of their backward (combine_bwd -> expert_ffn_bwd -> dispatch_bwd).
 
 The routing is given (not produced by the router), so these reach sizes and shapes the
 router's own limits keep out of the whole-layer tests: the largest expert count the
@@ -84,3 +85,60 @@ def test_given_routing_path(gpu_lib, kind, T, d, E, k, F):
          f"empty experts {int((np.diff(ref['expert_off']) == 0).sum())}; "
          f"y_disp err {e_yd:.2e}  y err {e_y:.2e}")
     assert e_yd <= BF16_TOL and e_y <= BF16_TOL
+
+
+BWD_CASES = [
+    # kind, T, d, E, k, F
+    ("random", 300, 64, 1024, 8, 64),     # the largest E: experts of 0-8 rows, many empty
+    ("same", 700, 128, 8, 3, 64),         # 700-row experts: long weight-gradient contractions
+    ("blocks", 1025, 128, 5, 1, 64),      # experts of 256 rows and one of 1 row
+]
+
+
+@pytest.mark.parametrize("kind,T,d,E,k,F", BWD_CASES,
+                         ids=[f"{c[0]}-T{c[1]}-d{c[2]}-E{c[3]}-k{c[4]}-F{c[5]}" for c in BWD_CASES])
+def test_given_routing_backward(gpu_lib, kind, T, d, E, k, F):
+    """combine_bwd -> expert_ffn_bwd -> dispatch_bwd after a forward with the same given
+    routing, against the oracle's transposes; experts without rows get zero weight
+    gradients, bit for bit."""
+    moe = gpu_lib
+    wl = moe_synth.small_workload(moe_synth.WORKLOADS["mid_bf16_train"], T=T, d=d, E=E, k=k, F=F)
+    _say(f"given routing backward {kind}: {wl}")
+    inp = moe_synth.layer_inputs(wl)
+    idx, gates = _routing(kind, T, E, k)
+    x, w13, w2 = inp["x"].cuda(), inp["w13"].cuda(), inp["w2"].cuda()
+    dy = moe_synth.upstream_grad(wl)
+    P = T * k
+    plan = moe.moe_dispatch(x, idx.cuda(), E)
+    hu = torch.empty((P, 2 * F), dtype=torch.bfloat16, device="cuda")
+    act = moe.moe_expert_ffn_gate_up(plan["x_disp"], plan["expert_off"], w13, hu_save=hu)
+    y_disp = moe.moe_expert_ffn_down(act, plan["expert_off"], w2)
+    dy_disp, dgates = moe.moe_combine_bwd(dy.cuda(), y_disp, plan["pair_slot"], gates.cuda())
+    dx_disp, dw13, dw2 = moe.moe_expert_ffn_bwd(plan["x_disp"], dy_disp, hu, plan["expert_off"],
+                                                w13, w2)
+    dx = moe.moe_dispatch_bwd(dx_disp, plan["pair_slot"])
+    torch.cuda.synchronize()
+
+    ref = oracle.plan(idx.numpy(), E)
+    assert np.array_equal(plan["pair_slot"].cpu().numpy(), ref["pair_slot"])
+    xd = oracle.dispatch(inp["x"], ref["pair_slot"], P)
+    yd = oracle.expert_ffn(xd, ref["expert_off"], inp["w13"], inp["w2"])
+    r_dyd, r_dg = oracle.combine_bwd(dy, yd, ref["pair_slot"], gates.numpy(), P)
+    r_dxd, r_dw13, r_dw2 = oracle.expert_ffn_bwd(xd, r_dyd, ref["expert_off"], inp["w13"],
+                                                 inp["w2"])
+    r_dx = oracle.dispatch_bwd(r_dxd, ref["pair_slot"])
+    errs = {
+        "dgates": oracle.normwise_rel_err(dgates.cpu().numpy(), r_dg),
+        "dy_disp": oracle.normwise_rel_err(dy_disp.float().cpu().numpy(), r_dyd),
+        "dx_disp": oracle.normwise_rel_err(dx_disp.float().cpu().numpy(), r_dxd),
+        "dw13": oracle.normwise_rel_err(dw13.cpu().numpy(), r_dw13),
+        "dw2": oracle.normwise_rel_err(dw2.cpu().numpy(), r_dw2),
+        "dx": oracle.normwise_rel_err(dx.float().cpu().numpy(), r_dx),
+    }
+    _say("  " + "  ".join(f"{n} {v:.2e}" for n, v in errs.items()))
+    bad = {n: v for n, v in errs.items() if not v <= BF16_TOL}
+    assert not bad, bad
+    empty = np.nonzero(np.diff(ref["expert_off"]) == 0)[0]
+    if empty.size:
+        assert torch.count_nonzero(dw13[torch.from_numpy(empty).cuda()]).item() == 0
+        assert torch.count_nonzero(dw2[torch.from_numpy(empty).cuda()]).item() == 0
