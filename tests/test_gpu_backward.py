@@ -1,6 +1,6 @@
 """GPU parity of the backward path (training step) against the CPU oracle.
 
-combine_bwd -> expert_ffn_bwd (dgrad + wgrad grouped GEMMs) -> route_bwd ->
+combine_bwd -> route_bwd -> expert_ffn_bwd (dgrad + wgrad grouped GEMMs) ->
 dispatch_bwd, driven through the C ABI, every gradient compared with
 oracle.backward (float64) within the bf16 bar: normwise relative error <= 2e-2.
 """
