@@ -6,7 +6,7 @@
 // SwiGLU without biases, h = X W1^T, u = X W3^T, a = silu(h) * u, y = a W2^T.
 //
 // bf16 path: v_mfma_f32_32x32x16_bf16, float32 accumulation. Workgroup tile 256 token
-// rows x 256 weight rows x 64 deep, eight wavefronts (each 128 token rows x 64 weight
+// rows x 256 weight rows x 64 deep, eight wavefronts (each four alternating 32-row token sub-tiles x 64 weight
 // rows). For the gate/up GEMM the 256 weight rows are 128 rows of W1 and the same 128
 // rows of W3, so the SwiGLU epilogue pairs h and u in registers and writes a (and h, u
 // when they are saved for the backward). Tiles are double-buffered in LDS with an XOR
@@ -30,8 +30,9 @@ enum { EPI_SWIGLU = 0, EPI_PLAIN = 1 };
 typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
 
 // Eight wavefronts, two per SIMD: wave w takes weight group w & 3 (64 weight rows)
-// and token group w >> 2 (128 token rows), so each SIMD holds one wave of each token
-// group and the MFMA work per SIMD is the same for any count of live token rows.
+// and token group w >> 2, the 32-row token sub-tiles (w >> 2) + 2i. Each SIMD holds
+// one wave of each token group, so the MFMA work per SIMD is the same for any count of
+// live token rows, and its two waves' shares differ by at most one sub-tile.
 constexpr int kFwdThreads = 512;
 constexpr int kLdsFwd = kLdsGemm;
 // Waves 0-3 issue every stage's direct loads (each the share of two waves) and alone
@@ -99,7 +100,7 @@ __device__ __forceinline__ void read_frags(const unsigned char *As, const unsign
     }
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
-        const int r = trow + i * 32 + (lane & 31);
+        const int r = trow + i * 64 + (lane & 31);
         tf[i] = *reinterpret_cast<const bf16x8 *>(As + r * 128 + ((kc ^ swz(r)) << 4));
     }
 }
@@ -126,7 +127,10 @@ __device__ __forceinline__ void run_item(unsigned char *lds, const GemmItem &it,
 #pragma unroll
     for (int s = 0; s < 2; ++s)
         brow[s] = (EPI == EPI_SWIGLU) ? s * 128 + wn * 32 : wn * 64 + s * 32;
-    const int trow = wm * 128;
+    // token sub-tiles alternate between the two groups (group wm takes 32-row
+    // sub-tiles wm, wm + 2, ...), so the two wavefronts of a SIMD get equal shares of
+    // a partly filled tile
+    const int trow = wm * 32;
 
     const int KT = K / BK;
     const bool loader = !SPLIT || wave < kLoaderWaves;
@@ -172,11 +176,11 @@ __device__ __forceinline__ void run_item(unsigned char *lds, const GemmItem &it,
     // direct epilogue: D = W_tile * X_tile^T, so lane l holds token column m = l & 31 and, for
     // v = 4g + q, weight row n = 8g + 4*(l >> 5) + q: four consecutive outputs of one
     // token row, stored as one 8-byte write per (sub-tile, g)
-    const int64_t mrow0 = it.m0 + trow + (lane & 31);
+    const int64_t mrow0 = it.m0 + trow + (lane & 31);   // sub-tile i at mrow0 + 64 i
     const int nl = 4 * (lane >> 5);
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
-        const int64_t m = mrow0 + i * 32;
+        const int64_t m = mrow0 + i * 64;
         if (m >= it.m_end) continue;
         if (EPI == EPI_SWIGLU) {
 #pragma unroll
@@ -218,12 +222,12 @@ __device__ __forceinline__ void run_item(unsigned char *lds, const GemmItem &it,
     }
 
     // split: epilogue through stage buffer 1 (64 KiB), CR token rows at a time. D = W_tile *
-    // X_tile^T: lane l holds token row trow + 32i + (l & 31) and, for v = 4g + q, weight
+    // X_tile^T: lane l holds token row trow + 64i + (l & 31) and, for v = 4g + q, weight
     // row 8g + 4 (l >> 5) + q of sub-tile s, four consecutive outputs of one token row
     // that go to LDS as one 8-byte bf16 piece. A chunk row is RP bytes: gate/up a (128
     // columns, 256 B), with h and u behind it when they are saved; down 256 columns
-    // (512 B). Its 16-byte piece p sits at p ^ (row & 15). Chunks holding the storing
-    // waves' token half go first, so those waves hold fewer accumulators while storing.
+    // (512 B). Its 16-byte piece p sits at p ^ (row & 15). Chunks are taken starting
+    // half-way through the tile.
     const bool save = (EPI == EPI_SWIGLU) && hu_save != nullptr;
     const int RP = (EPI == EPI_SWIGLU) ? (save ? 768 : 256) : 512;
     const int CR = (EPI == EPI_SWIGLU) ? (save ? 64 : 256) : 128;
@@ -235,7 +239,7 @@ __device__ __forceinline__ void run_item(unsigned char *lds, const GemmItem &it,
         const int lo = c * CR;                               // first tile row of the chunk
 #pragma unroll
         for (int i = 0; i < NW; ++i) {
-            const int t0 = trow + 32 * i;
+            const int t0 = trow + 64 * i;
             if (t0 < lo || t0 >= lo + CR) continue;
             const int rl = t0 - lo + (lane & 31);
             unsigned char *row = cb + rl * RP + (lane >> 5) * 8;
@@ -393,7 +397,7 @@ __global__ __launch_bounds__(kFwdThreads) void k_gemm_bf16(
                                   wave, lane);
         // live 32-row token sub-tiles of this wave's token group
         const int nsub = int(min<int64_t>(8, (it.m_end - it.m0 + 31) / 32));
-        const int nw = min(4, max(0, nsub - (wave >> 2) * 4));
+        const int nw = min(4, max(0, (nsub - (wave >> 2) + 1) / 2));
         switch (nw) {
         case 4: run_item<EPI, 4, SPLIT>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
         case 3: run_item<EPI, 3, SPLIT>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
