@@ -251,7 +251,7 @@ __device__ __forceinline__ void mma_bwd_stage(const unsigned char *buf, int arow
 #pragma unroll
             for (int s = 0; s < 2; ++s) wf[0][s] = frag<true>(As, arow + s * 32, 0, lane);
 #pragma unroll
-            for (int i = 0; i < NW; ++i) tf[0][i] = frag<BTR>(Bs, brow + i * 32, 0, lane);
+            for (int i = 0; i < NW; ++i) tf[0][i] = frag<BTR>(Bs, brow + i * 64, 0, lane);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (ks + 1 < BK / 16) {
@@ -259,7 +259,7 @@ __device__ __forceinline__ void mma_bwd_stage(const unsigned char *buf, int arow
 #pragma unroll
             for (int s = 0; s < 2; ++s) wf[n][s] = frag<true>(As, arow + s * 32, ks + 1, lane);
 #pragma unroll
-            for (int i = 0; i < NW; ++i) tf[n][i] = frag<BTR>(Bs, brow + i * 32, ks + 1, lane);
+            for (int i = 0; i < NW; ++i) tf[n][i] = frag<BTR>(Bs, brow + i * 64, ks + 1, lane);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -396,7 +396,10 @@ __device__ __forceinline__ void run_bwd_item(unsigned char *lds, const BwdArgs &
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-    const int arow = wn * 64, brow = wm * 128;
+    // output-row sub-tiles alternate between the two groups (group wm takes 32-row
+    // sub-tiles wm, wm + 2, ...), so a SIMD's two wavefronts share a partly filled tile
+    // evenly
+    const int arow = wn * 64, brow = wm * 32;
 
     // stage 0 was issued before the previous item's epilogue (or before the first item)
     if (loader) __builtin_amdgcn_s_waitcnt(0);
@@ -417,30 +420,22 @@ __device__ __forceinline__ void run_bwd_item(unsigned char *lds, const BwdArgs &
     }
 
     // epilogue through stage buffer 1, 64 tile rows at a time. The accumulators of lane l
-    // are tile row brow + 32i + (l & 31) and, for v = 4g + q, tile column arow + 32s + 8g +
-    // 4 (l >> 5) + q. Chunk c = tile rows 64c..64c+63, held by the waves of half c >> 1
-    // (sub-tiles 2 (c & 1) and 2 (c & 1) + 1); chunks 2 and 3 go first, so the storing
-    // waves hold no accumulators any more when chunks 0 and 1 are stored.
+    // are tile row brow + 64i + (l & 31) and, for v = 4g + q, tile column arow + 32s + 8g +
+    // 4 (l >> 5) + q. Chunk c = tile rows 64c..64c+63 = sub-tile i = c of both groups.
     unsigned char *cb = lds + (kLdsA + kLdsB);
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-        const int c = cc ^ 2;
-        if (wm == (c >> 1)) {
+    for (int c = 0; c < 4; ++c) {
+        if (c < NW) {
+            const int rl = 32 * wm + (lane & 31);
 #pragma unroll
-            for (int ii = 0; ii < 2; ++ii) {
-                const int i = 2 * (c & 1) + ii;
-                if (i >= NW) continue;
-                const int rl = 32 * ii + (lane & 31);
+            for (int s = 0; s < 2; ++s)
 #pragma unroll
-                for (int s = 0; s < 2; ++s)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int pc = wn * 16 + 8 * s + 2 * g + (lane >> 5);
-                        *reinterpret_cast<float4 *>(cb + rl * 1024 + ((pc ^ (rl & 15)) << 4)) =
-                            make_float4(acc[i][s][4 * g], acc[i][s][4 * g + 1], acc[i][s][4 * g + 2],
-                                        acc[i][s][4 * g + 3]);
-                    }
-            }
+                for (int g = 0; g < 4; ++g) {
+                    const int pc = wn * 16 + 8 * s + 2 * g + (lane >> 5);
+                    *reinterpret_cast<float4 *>(cb + rl * 1024 + ((pc ^ (rl & 15)) << 4)) =
+                        make_float4(acc[c][s][4 * g], acc[c][s][4 * g + 1], acc[c][s][4 * g + 2],
+                                    acc[c][s][4 * g + 3]);
+                }
         }
         __syncthreads();
         if (!loader) {
@@ -484,7 +479,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_gemm_bwd(BwdArgs A, int t_tiles
         int nsub;
         if (DGRAD) nsub = int(min<int64_t>(8, (it.m_end - it.m0 + 31) / 32));
         else nsub = min(8, (((KIND == G3_DW2) ? A.d : 2 * A.F) - it.b0 + 31) / 32);
-        const int nw = min(4, max(0, nsub - (wave >> 2) * 4));
+        const int nw = min(4, max(0, (nsub - (wave >> 2) + 1) / 2));
         switch (nw) {
         case 4: run_bwd_item<KIND, 4>(lds, A, it, next, has_next ? nitem : -1, tile_off, t_tiles, n_tiles, wave, lane); break;
         case 3: run_bwd_item<KIND, 3>(lds, A, it, next, has_next ? nitem : -1, tile_off, t_tiles, n_tiles, wave, lane); break;
