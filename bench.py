@@ -3,19 +3,21 @@
 
 Headline step = one forward pass of the layer over one batch of synthetic tokens
 already resident in HBM: moe_route -> moe_dispatch -> moe_expert_ffn_gate_up ->
-moe_expert_ffn_down -> moe_combine (all libmoe HIP kernels), on the T=4096, d=2048,
-E=64, k=6, F=1408 bf16 layer. The same JSON line also reports:
+moe_expert_ffn_down -> moe_combine (all libmoe HIP kernels), on the largest layer that
+fits one GPU: T=8192, d=7168, E=384, k=8, F=2048 bf16 (34 GB of expert weights
+resident). The same JSON line also reports:
+  mid          the T=4096, d=2048, E=64, k=6, F=1408 layer forward, with its own
+               roofline line,
   train_step   forward + backward of that layer (combine_bwd, route_bwd,
                expert_ffn_bwd, dispatch_bwd) on the same shapes,
   ep_dispatch_combine  the rank-major dispatch and combine of 32 source ranks x 128
                tokens, d=7168, E=384, k=8, Zipf(1.2) routing (identity experts), and
                destination 0's receive path (reorder, 12-expert SwiGLU GEMM, scatter),
-  large        the T=8192, d=7168, E=384, k=8, F=2048 layer forward (34 GB weights),
-  overlap      the headline layer with a shared expert on a second stream, and with two
+  overlap      the mid layer with a shared expert on a second stream, and with two
                micro-batches on two streams, each against its one-stream form,
   roofline     the dominant kernel of the headline step, timed live with HIP events,
-  cpu_baseline the CPU oracle on the host cores over whole passes of the headline
-               workload.
+  cpu_baseline the CPU oracle on the host cores over a bounded sample of the headline
+               workload, scaled to the whole batch.
 
 Prints ONE JSON line.
 """
@@ -43,14 +45,15 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mid_bf16", choices=["mid_bf16", "large_bf16", "tiny_f32"],
+    ap.add_argument("--workload", default="large_bf16", choices=["large_bf16", "mid_bf16", "tiny_f32"],
                     help="workload of the headline forward step")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-extras", action="store_true",
-                    help="headline only (no train step, EP dispatch/combine or large layer)")
-    ap.add_argument("--no-large", action="store_true", help="skip the 34 GB large-layer run")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="headline only (no mid layer, train step, EP dispatch/combine or overlap)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--only-mid", action="store_true",
+                    help="run only the T=4096 d=2048 E=64 layer forward (for profiler runs)")
     ap.add_argument("--only-overlap", action="store_true",
                     help="run only the two-stream shared-expert and micro-batch forms")
     ap.add_argument("--only-ep", action="store_true",
@@ -407,10 +410,20 @@ def overlap_bench(torch, moe, wl, dev, steps, warmup):
     return res
 
 
-def cpu_baseline(wl, inp, target_s):
-    """The oracle as it is, on the host cores, over whole passes of the workload."""
+def _oracle_threads():
     import threadpoolctl
     import oracle
+    threads = [oracle.num_threads()]
+    threads += [p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()]
+    return int(max(threads))
+
+
+def cpu_baseline(wl, inp, target_s):
+    """The oracle as it is, on the host cores, over whole passes of the workload (small
+    layers), or over a bounded sample of one pass (the large layer, see below)."""
+    import oracle
+    if wl.T * wl.d * wl.E * max(wl.F, 1) > 4096 * 2048 * 64 * 1408:
+        return cpu_baseline_sampled(wl, inp, target_s)
     host = {n: t.cpu() for n, t in inp.items()}
     n, total = 0, 0.0
     while n < 10 and (total < target_s or n == 0):
@@ -418,12 +431,59 @@ def cpu_baseline(wl, inp, target_s):
         oracle.forward(host["x"], host["w_router"], host["w13"], host["w2"], wl.k)
         total += time.perf_counter() - t0
         n += 1
-    threads = [oracle.num_threads()]
-    threads += [p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()]
-    return {"value": round(n * wl.T / total, 2), "unit": "tokens/s", "cores": int(max(threads)),
+    return {"value": round(n * wl.T / total, 2), "unit": "tokens/s", "cores": _oracle_threads(),
             "kind": "oracle",
             "sample": f"{n} full forward pass(es) of the {wl.T}-token workload "
                       f"({total:.1f} s; float64 numpy FFN, float32 C router)"}
+
+
+def cpu_baseline_sampled(wl, inp, target_s):
+    """One oracle forward of the large layer is minutes of host work (5.8 TFLOP of
+    float64 expert GEMMs), so it is sampled: the oracle's own steps run in its order on
+    the whole batch (route, plan, dispatch, combine), and its expert FFN on whole
+    experts, evenly spaced over the expert ids, until about target_s seconds; the FFN
+    time is scaled by E / experts sampled. Each sampled expert's weights are copied to
+    the host when its turn comes (the oracle widens them to float64 itself)."""
+    import numpy as np
+    import oracle
+    x_h, wr_h = inp["x"].cpu(), inp["w_router"].cpu()
+    t = {}
+    t0 = time.perf_counter()
+    _, idx, gates = oracle.route(x_h, wr_h, wl.k)
+    t["route"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    p = oracle.plan(idx, wl.E)
+    t["plan"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    x_disp = oracle.dispatch(x_h, p["pair_slot"], wl.T * wl.k)
+    t["dispatch"] = time.perf_counter() - t0
+    off = p["expert_off"]
+    y_disp = np.zeros((x_disp.shape[0], wl.d), dtype=np.float64)
+    order = [int(e) for e in np.linspace(0, wl.E - 1, 64).round()]
+    done, t_ffn, rows = 0, 0.0, 0
+    for e in order:
+        a, b = int(off[e]), int(off[e + 1])
+        w13_e, w2_e = inp["w13"][e].cpu(), inp["w2"][e].cpu()
+        t0 = time.perf_counter()
+        if b > a:
+            y_disp[a:b] = oracle.swiglu_expert(x_disp[a:b], w13_e, w2_e)
+        t_ffn += time.perf_counter() - t0
+        done += 1
+        rows += b - a
+        if done >= 2 and t_ffn + sum(t.values()) >= target_s:
+            break
+    t["expert_ffn"] = t_ffn * wl.E / done
+    t0 = time.perf_counter()
+    oracle.combine(y_disp, p["pair_slot"], gates)
+    t["combine"] = time.perf_counter() - t0
+    total = sum(t.values())
+    return {"value": round(wl.T / total, 3), "unit": "tokens/s", "cores": _oracle_threads(),
+            "kind": "oracle",
+            "sample": f"one forward of the {wl.T}-token batch: route, plan, dispatch and combine "
+                      f"on every token ({t['route'] + t['plan'] + t['dispatch'] + t['combine']:.1f} s), "
+                      f"the expert FFN on {done} of {wl.E} experts ({rows} rows, {t_ffn:.1f} s) "
+                      f"scaled by {wl.E}/{done} to {t['expert_ffn']:.0f} s; float64 numpy FFN, "
+                      f"float32 C router"}
 
 
 # Sources that define the grouped-GEMM kernels; a traffic record taken with other
@@ -431,7 +491,19 @@ def cpu_baseline(wl, inp, target_s):
 KERNEL_SOURCES = ("token_routing_expert_router_amd/csrc/ffn.hip",
                   "token_routing_expert_router_amd/csrc/gemm_common.h",
                   "token_routing_expert_router_amd/csrc/common.h")
-TRAFFIC_RECORD = "profiles/gate_up_T4096_d2048_E64_k6_F1408_hbm_traffic.json"
+
+
+def shape_tag(wl):
+    return f"T{wl.T}_d{wl.d}_E{wl.E}_k{wl.k}_F{wl.F}"
+
+
+def workload_desc(wl):
+    return f"T={wl.T} d={wl.d} E={wl.E} k={wl.k} F={wl.F} {wl.dtype}"
+
+
+def traffic_record_path(kernel, wl):
+    """The committed FETCH_SIZE / WRITE_SIZE record of one kernel on one workload."""
+    return os.path.join(ROOT, "profiles", f"{kernel}_{shape_tag(wl)}_hbm_traffic.json")
 
 
 def kernel_source_digest():
@@ -443,15 +515,17 @@ def kernel_source_digest():
     return h.hexdigest()
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE record,
-    or None if there is none for it or the kernel sources changed since it was taken."""
-    path = os.path.join(ROOT, TRAFFIC_RECORD)
+def measured_traffic(kernel, wl):
+    """HBM bytes per launch of `kernel` on workload `wl` from the committed FETCH_SIZE /
+    WRITE_SIZE record, or None if there is none for this kernel AND workload, or the
+    kernel sources changed since it was taken."""
+    path = traffic_record_path(kernel, wl)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("stage") != kernel or rec.get("source_sha256") != kernel_source_digest():
+    if (rec.get("stage") != kernel or rec.get("workload") != workload_desc(wl)
+            or rec.get("source_sha256") != kernel_source_digest()):
         return None
     return int(rec["traffic_bytes_per_launch"])
 
@@ -498,23 +572,10 @@ def main():
         print(json.dumps({"train_step": ts}), flush=True)
         return
     wl = moe_synth.WORKLOADS[args.workload]
+    if args.only_mid:
+        wl = moe_synth.WORKLOADS["mid_bf16"]
     inp, elapsed, stages = forward_bench(torch, moe, wl, dev, args.steps, args.warmup)
     T, k, E, F, d = wl.T, wl.k, wl.E, wl.F, wl.d
-
-    work = stage_work(wl)
-    dom = max(stages, key=lambda n: stages[n]["us"])
-    w = work[dom]
-    bound = stages[dom]["bound"]
-    t = stages[dom]["us"] * 1e-6
-    if bound == "hbm":
-        achieved, peak, unit, per = w["bytes"] / t / 1e9, PEAK_HBM_GBS, "GB/s", w["bytes"]
-    else:
-        peak = PEAKS[bound]
-        achieved, unit, per = w["flops"] / t / 1e12, "TFLOP/s", w["flops"]
-    roofline = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": measured_traffic(dom), "kernel": dom,
-                "per_launch": per}
-
     line = {
         "metric": METRIC,
         "value": round(T * args.steps / elapsed, 1),
@@ -528,35 +589,56 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": f"{wl.name}: MoE layer forward T={T} d={d} E={E} k={k} F={F} "
-                               f"{wl.dtype}, softmax top-{k} gating, SwiGLU experts",
+        "config": {"workload": f"{wl.name}: MoE layer forward {workload_desc(wl)}, softmax "
+                               f"top-{k} gating, SwiGLU experts",
                    "T": T, "d": d, "E": E, "k": k, "F": F, "parallelism": "none (1 GPU)"},
         "stages": stages,
-        "roofline": roofline,
+        "roofline": roofline_of(wl, stages),
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
     del inp
     torch.cuda.empty_cache()
-    if not args.no_extras and wl.dtype == "bf16":
+    if not args.no_extras and not args.only_mid and wl.dtype == "bf16":
+        mwl = moe_synth.WORKLOADS["mid_bf16"]
+        minp, mel, mst = forward_bench(torch, moe, mwl, dev, args.steps, args.warmup)
+        del minp
+        torch.cuda.empty_cache()
+        line["mid"] = {"workload": f"{mwl.name}: MoE layer forward {workload_desc(mwl)}",
+                       "value": round(mwl.T * args.steps / mel, 1), "unit": "tokens/s",
+                       "ms_per_step": round(mel / args.steps * 1e3, 4), "steps": args.steps,
+                       "stages": mst, "roofline": roofline_of(mwl, mst)}
         line["train_step"] = train_bench(torch, moe, moe_synth.WORKLOADS["mid_bf16_train"], dev,
                                          max(5, args.steps // 2), max(2, args.warmup // 2))
         torch.cuda.empty_cache()
         line["ep_dispatch_combine"] = ep_bench(torch, moe, moe_synth.WORKLOADS["ep32_zipf"], dev,
                                                max(5, args.steps // 2), max(2, args.warmup // 2))
         torch.cuda.empty_cache()
-        line["overlap"] = overlap_bench(torch, moe, wl, dev, max(5, args.steps // 2),
+        line["overlap"] = overlap_bench(torch, moe, mwl, dev, max(5, args.steps // 2),
                                         max(2, args.warmup // 2))
-        if not args.no_large:
-            lwl = moe_synth.WORKLOADS["large_bf16"]
-            linp, lel, lst = forward_bench(torch, moe, lwl, dev, 5, 2)
-            del linp
-            torch.cuda.empty_cache()
-            line["large"] = {"workload": f"{lwl.name}: MoE layer forward T={lwl.T} d={lwl.d} "
-                                         f"E={lwl.E} k={lwl.k} F={lwl.F} bf16, 34 GB weights",
-                             "value": round(lwl.T * 5 / lel, 1), "unit": "tokens/s",
-                             "ms_per_step": round(lel / 5 * 1e3, 4), "steps": 5, "stages": lst}
     print(json.dumps(line), flush=True)
+
+
+def roofline_of(wl, stages):
+    """The dominant stage's kernel against its roofline: algorithmic bytes (or flops) per
+    launch over its event-timed average duration."""
+    work = stage_work(wl)
+    dom = max(stages, key=lambda n: stages[n]["us"])
+    w = work[dom]
+    bound = stages[dom]["bound"]
+    t = stages[dom]["us"] * 1e-6
+    if bound == "hbm":
+        achieved, peak, unit, per = w["bytes"] / t / 1e9, PEAK_HBM_GBS, "GB/s", w["bytes"]
+    else:
+        peak = PEAKS[bound]
+        achieved, unit, per = w["flops"] / t / 1e12, "TFLOP/s", w["flops"]
+    out = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+           "frac": round(achieved / peak, 4), "traffic": measured_traffic(dom, wl), "kernel": dom,
+           "per_launch": per}
+    if w["flops"]:
+        out["mfma_frac"] = round(w["flops"] / t / 1e12 / PEAK_BF16_TFLOPS, 4)
+        out["hbm_frac"] = round(w["bytes"] / t / 1e9 / PEAK_HBM_GBS, 4)
+    return out
 
 
 if __name__ == "__main__":

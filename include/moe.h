@@ -12,8 +12,10 @@
  * Conventions shared by every call
  * --------------------------------
  * - Memory: every pointer argument is DEVICE memory owned by the caller (allocate
- *   it with hipMalloc or any device allocator). The library allocates nothing and
- *   keeps no mutable global state; scratch space comes in through `ws`.
+ *   it with hipMalloc or any device allocator). The library allocates nothing;
+ *   scratch space comes in through `ws`. Its only process-wide state is one-time
+ *   set-up per device (kernel LDS limits, the compute-unit count), done on a device's
+ *   first call under std::call_once, so concurrent first calls are safe.
  * - Layout: all matrices are row-major and dense. A "row" of a token tensor is
  *   d contiguous elements. Rows and pointers must be 16-byte aligned
  *   (d * element size % 16 == 0, pointers % 16 == 0); otherwise MOE_ERR_ALIGN.
@@ -78,6 +80,21 @@ typedef struct moe_layout {
 int32_t     moe_abi_version(void);
 const char *moe_status_str(moe_status_t status);
 
+/* Workspace bytes of one call, by operation (the per-call functions below give the
+ * same numbers): MOE_OP_DISPATCH for moe_dispatch / moe_dispatch_fp8 (uses T, E, k,
+ * layout), MOE_OP_EXPERT_FFN for moe_expert_ffn and MOE_OP_EXPERT_FFN_BWD for
+ * moe_expert_ffn_bwd (use E, rows, d, F, dtype). Arguments an operation does not use
+ * are ignored. Every other call needs no workspace (0). Invalid sizes give 0.
+ * [EFA] NVSHMEM-based pplx-kernels: one interface, whatever moves the bytes; the
+ * caller sizes every buffer up front, once. */
+typedef int32_t moe_op_t;
+#define MOE_OP_DISPATCH        0
+#define MOE_OP_EXPERT_FFN      1
+#define MOE_OP_EXPERT_FFN_BWD  2
+size_t moe_workspace_size(moe_op_t op, int64_t T, int32_t E, int32_t k,
+                          const struct moe_layout *layout, int64_t rows, int64_t d, int64_t F,
+                          moe_dtype_t dtype);
+
 /* ------------------------------------------------------------------ router
  * [EFA] Introduction: a small linear routing layer decides which experts multiply a
  * token; [EFA] Send and receive buffers: each token goes to R (here k) of E experts.
@@ -92,9 +109,10 @@ const char *moe_status_str(moe_status_t status);
  *   reading that makes the gate-weighted average of combine a true average.
  *
  * x [T,d] dtype, w_router [E,d] dtype; logits [T,E] f32 (NULL: not written);
- * topk_idx [T,k] int32; topk_w [T,k] f32. Limits: 1 <= k <= min(E, 32), E <= 512;
- * for bf16 also d <= 2^26 and E*d*2 < 2^31 bytes (32-bit buffer offsets), else
- * MOE_ERR_UNSUPPORTED before anything is launched. T = 0 is a no-op. */
+ * topk_idx [T,k] int32; topk_w [T,k] f32. Limits: 1 <= k <= min(E, 32); E <= 1024
+ * for bf16, E <= 512 for f32; for bf16 also d <= 2^26 and E*d*2 < 2^31 bytes (32-bit
+ * buffer offsets), else MOE_ERR_UNSUPPORTED before anything is launched. T = 0 is a
+ * no-op. */
 moe_status_t moe_route(const void *x, const void *w_router, int64_t T, int64_t d, int32_t E,
                        int32_t k, moe_dtype_t dtype, int32_t flags, float *logits,
                        int32_t *topk_idx, float *topk_w, void *stream);
@@ -127,7 +145,15 @@ moe_status_t moe_route(const void *x, const void *w_router, int64_t T, int64_t d
  * cap_rows_per_dst >= (T/n_src) * n_src * min(k, E/n_dst) (the tight form of the
  * article's bound: a token sends at most min(k, E/N) rows to one destination).
  * Tokens must list k distinct experts in [0, E); violations raise the device flag.
- * Limits: E <= 1024, k <= 32.
+ * Limits: E <= 1024, k <= 32, T*k < 2^31, n_dst*cap < 2^31. The rank-major layout
+ * (n_src or n_dst > 1) also scans its plan in one workgroup's LDS: it needs
+ *   B*E + n_src*E + E + 1 + n_dst*(n_src+1) + n_src*n_dst <= 32768 ints,
+ * B = n_src * ceil(T/n_src / 256) plan blocks (e.g. 32 sources x 128 tokens at E = 384
+ * uses 25,665); larger plans return MOE_ERR_UNSUPPORTED. The expert-major layout has
+ * no such limit.
+ * T = 0 (an empty batch): topk_idx, pair_slot, x and x_disp are not read; counts,
+ * expert_off and chunk_off are written as zeros, every row_pair entry as -1, and the
+ * status flag is cleared.
  * ws: at least moe_dispatch_workspace_size() bytes, 256-byte aligned; its first
  * bytes hold the device status flag that moe_dispatch_status() reads. */
 size_t moe_dispatch_workspace_size(int64_t T, int32_t E, int32_t k, const moe_layout_t *layout);
@@ -287,7 +313,8 @@ moe_status_t moe_combine_partials(const void *partial, const int32_t *pair_slot,
  *                   d and F multiples of 64, 2F * d * 2 bytes < 2^31, E <= 1024;
  *                   otherwise MOE_ERR_UNSUPPORTED. Every dw13/dw2 entry is written,
  *                   zeros for experts without rows.
- * moe_route_bwd:   dlogits_sel[t,j] = g_j (dg_j - sum_i g_i dg_i)   (f32, RENORM gating)
+ * moe_route_bwd:   (T = 0: only dw_router is written, as zeros; nothing else is read)
+ *                   dlogits_sel[t,j] = g_j (dg_j - sum_i g_i dg_i)   (f32, RENORM gating)
  *                   dw_router[e,:] = sum over the rows of expert e in the expert-major
  *                                    plan (expert_off, row_pair from moe_dispatch),
  *                                    i.e. over its tokens, of

@@ -562,3 +562,20 @@ def normwise_rel_err(got, ref) -> float:
     scale = float(np.max(np.abs(ref)))
     diff = float(np.max(np.abs(got - ref)))
     return diff / scale if scale > 0 else diff
+
+
+def elementwise_rel_err(got, ref) -> float:
+    """max_i |got_i - ref_i| / (|ref_i| + rms(ref)) (0 for two empty arrays): the
+    elementwise reading of a relative-error bar. The rms term keeps outputs near zero
+    from dividing by almost nothing (every output here is a sum of many products, so
+    some sit at zero by chance)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if ref.size == 0:
+        return 0.0
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    den = np.abs(ref) + rms
+    diff = np.abs(got - ref)
+    if rms == 0.0:
+        return float(np.max(diff))
+    return float(np.max(diff / den))

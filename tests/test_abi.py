@@ -59,7 +59,8 @@ def test_route_host_validation(lib):
     assert r(FAKE, FAKE, 10, (1 << 26) + 8, 8, 2, BF16, 0, None, FAKE, FAKE, None) == UNSUPPORTED
     assert r(FAKE, FAKE, 10, 1 << 22, 512, 2, BF16, 0, None, FAKE, FAKE, None) == UNSUPPORTED
     assert r(None, FAKE, 10, 64, 8, 2, BF16, 0, None, FAKE, FAKE, None) == INVALID
-    assert r(FAKE, FAKE, 10, 64, 600, 2, BF16, 0, None, FAKE, FAKE, None) == UNSUPPORTED
+    assert r(FAKE, FAKE, 10, 64, 1100, 2, BF16, 0, None, FAKE, FAKE, None) == UNSUPPORTED
+    assert r(FAKE, FAKE, 10, 64, 600, 2, F32, 0, None, FAKE, FAKE, None) == UNSUPPORTED
     assert r(FAKE, FAKE, 10, 64, 64, 33, BF16, 0, None, FAKE, FAKE, None) == UNSUPPORTED
     assert r(None, None, 0, 64, 8, 2, BF16, 0, None, None, None, None) == OK          # empty
 
@@ -161,3 +162,66 @@ def test_combine_add_host_validation(lib):
     a = lib.moe_combine_add
     assert a(FAKE, FAKE, FAKE, 10, 2, 64, 20, BF16, None, FAKE, None) == INVALID     # residual
     assert a(FAKE, FAKE, FAKE, 10, 2, 64, 20, BF16, FAKE + 8, FAKE, None) == ALIGN
+
+
+def test_expert_major_dispatch_accepts_large_batches(lib):
+    """The expert-major plan scan walks its blocks in batches and has no LDS limit, so
+    large prefill batches pass every host check. Each case runs up to the workspace-size
+    check, which comes after the shape checks, and gives that check's code; so no call
+    here reaches a launch."""
+    d = lib.moe_dispatch
+    for T, E, k in ((16384, 512, 8), (32768, 384, 8), (8192, 1024, 8), (262144, 64, 6)):
+        ws_sz = lib.moe_dispatch_workspace_size(T, E, k, None)
+        assert ws_sz > 0
+        st = d(FAKE, FAKE, T, 7168, E, k, BF16, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+               ws_sz - 1, None)
+        assert st == CAPACITY, (T, E, k, st)
+    # the rank-major scan keeps its whole plan in one workgroup's LDS (32768 ints):
+    # 64 sources of 4096 tokens at E = 1024 need 1024 blocks x 1024 experts of it
+    lay = _layout(64, 64, 64 * 4096 * 16)
+    ws_sz = lib.moe_dispatch_workspace_size(64 * 4096, 1024, 8, lay)
+    st = d(FAKE, FAKE, 64 * 4096, 64, 1024, 8, BF16, lay, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+           ws_sz, None)
+    assert st == UNSUPPORTED
+
+
+def test_empty_batch_plan_host_validation(lib):
+    """T = 0: the plan outputs are still written (zeros, row_pair -1), so they and the
+    workspace must be given; topk_idx, pair_slot, x and x_disp are not needed."""
+    d = lib.moe_dispatch
+    ws_sz = lib.moe_dispatch_workspace_size(0, 8, 2, None)
+    assert ws_sz > 0
+    assert d(None, None, 0, 64, 8, 2, BF16, None, None, FAKE, FAKE, None, None, None, FAKE,
+             ws_sz, None) == INVALID                       # no counts
+    assert d(None, None, 0, 64, 8, 2, BF16, None, FAKE, FAKE, FAKE, None, None, None, FAKE + 16,
+             ws_sz, None) == ALIGN                         # workspace not 256-byte aligned
+    lay = _layout(4, 4, 100)
+    assert d(None, None, 0, 64, 8, 2, BF16, lay, FAKE, FAKE, FAKE, None, None, None, FAKE,
+             ws_sz, None) == INVALID                       # 400 rows but no row_pair
+    rb = lib.moe_route_bwd
+    assert rb(None, None, None, None, None, None, 0, 64, 8, 2, BF16, None, None, None) == INVALID
+    assert rb(None, None, None, None, None, None, 0, 64, 8, 2, BF16, None, FAKE + 8,
+              None) == ALIGN
+
+
+def test_workspace_size_by_operation(lib):
+    lay = _layout(32, 32, 49152)
+    ws = lib.moe_workspace_size
+    assert ws(0, 4096, 384, 8, lay, 0, 0, 0, BF16) == lib.moe_dispatch_workspace_size(4096, 384, 8, lay)
+    assert ws(0, 4096, 64, 6, None, 0, 0, 0, BF16) == lib.moe_dispatch_workspace_size(4096, 64, 6, None)
+    assert ws(1, 0, 64, 0, None, 24576, 2048, 1408, BF16) == \
+        lib.moe_expert_ffn_workspace_size(64, 24576, 2048, 1408, BF16)
+    assert ws(2, 0, 64, 0, None, 24576, 2048, 1408, BF16) == \
+        lib.moe_expert_ffn_bwd_workspace_size(64, 24576, 2048, 1408, BF16)
+    assert ws(1, 0, 64, 0, None, 24576, 2048, 1408, BF16) > 0
+    assert ws(7, 4096, 64, 6, None, 24576, 2048, 1408, BF16) == 0      # no such operation
+    assert ws(0, -1, 64, 6, None, 0, 0, 0, BF16) == 0                 # invalid sizes
+
+
+def test_route_accepts_1024_experts_in_bf16(lib):
+    r = lib.moe_route
+    # past every argument check, the null logits/idx pointers are the only fault:
+    # E = 1024 is accepted for bf16 (INVALID from the null topk_idx), refused for f32
+    assert r(FAKE, FAKE, 10, 64, 1024, 8, BF16, 0, None, None, FAKE, None) == INVALID
+    assert r(FAKE, FAKE, 10, 64, 1024, 8, F32, 0, None, None, FAKE, None) == UNSUPPORTED
+    assert r(FAKE, FAKE, 10, 64, 1025, 8, BF16, 0, None, None, FAKE, None) == UNSUPPORTED

@@ -39,12 +39,14 @@ def _compare(wl, inp, dy, fwd, bwd, tol=BF16_TOL):
     ref = oracle.backward(host["x"], host["w_router"], host["w13"], host["w2"], dy.cpu(), wl.k)
     assert np.array_equal(fwd["topk_idx"].cpu().numpy(), ref["idx"])
     assert np.array_equal(fwd["pair_slot"].cpu().numpy(), ref["pair_slot"])
-    errs = {}
+    errs, eerrs = {}, {}
     for mine, theirs in (("dgates", "dgates"), ("dy_disp", "dy_disp"), ("dx_disp", "dx_disp"),
                          ("dw13", "dw13"), ("dw2", "dw2"), ("dlogits_sel", "dlogits_sel"),
                          ("dw_router", "dw_router"), ("dx", "dx")):
         errs[mine] = oracle.normwise_rel_err(_np(bwd[mine]), ref[theirs])
-    _say("  " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+        eerrs[mine] = oracle.elementwise_rel_err(_np(bwd[mine]), ref[theirs])
+    _say("  normwise    " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    _say("  elementwise " + "  ".join(f"{k} {v:.2e}" for k, v in eerrs.items()))
     bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, bad
     return ref

@@ -142,3 +142,40 @@ def test_given_routing_backward(gpu_lib, kind, T, d, E, k, F):
     if empty.size:
         assert torch.count_nonzero(dw13[torch.from_numpy(empty).cuda()]).item() == 0
         assert torch.count_nonzero(dw2[torch.from_numpy(empty).cuda()]).item() == 0
+
+
+@pytest.mark.parametrize("layout", [None, (4, 4, 64)], ids=["expert-major", "rank-major"])
+def test_empty_batch_writes_an_empty_plan(gpu_lib, layout):
+    """T = 0: the plan outputs describe an empty batch whatever the buffers held before
+    (zero counts and offsets, every row unused, the flag clear), and the router's
+    backward gives a zero weight gradient without reading a plan."""
+    moe = gpu_lib
+    E, k, d = 16, 2, 64
+    lay = moe.Layout(*layout) if layout else None
+    n_src, n_dst, cap = layout if layout else (1, 1, 0)
+    dev = "cuda"
+    lib = moe.load()
+    ws = torch.full((max(256, int(lib.moe_dispatch_workspace_size(0, E, k, None))),), 0x55,
+                    dtype=torch.uint8, device=dev)
+    counts = torch.full((n_src, E), 7, dtype=torch.int32, device=dev)
+    expert_off = torch.full((E + 1,), 7, dtype=torch.int32, device=dev)
+    chunk_off = torch.full((n_dst, n_src + 1), 7, dtype=torch.int32, device=dev)
+    row_pair = torch.full((max(1, n_dst * cap),), 7, dtype=torch.int32, device=dev)
+    import ctypes
+    clay = lay._c() if lay else None
+    st = lib.moe_dispatch(None, None, 0, d, E, k, 1, ctypes.byref(clay) if clay else None,
+                          counts.data_ptr(), expert_off.data_ptr(), chunk_off.data_ptr(), None,
+                          row_pair.data_ptr(), None, ws.data_ptr(), ws.numel(),
+                          torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    assert moe.moe_dispatch_status(ws) == 0
+    assert int(counts.abs().sum()) == 0 and int(expert_off.abs().sum()) == 0
+    assert int(chunk_off.abs().sum()) == 0
+    if cap:
+        assert bool((row_pair == -1).all())
+    dwr = torch.full((E, d), float("nan"), dtype=torch.float32, device=dev)
+    st = lib.moe_route_bwd(None, None, None, None, None, None, 0, d, E, k, 1, None,
+                           dwr.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(dwr)) == 0

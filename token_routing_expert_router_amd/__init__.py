@@ -17,7 +17,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["MoEError", "load", "library_path", "moe_abi_version", "moe_route", "moe_dispatch",
+__all__ = ["MoEError", "load", "library_path", "moe_abi_version", "moe_workspace_size",
+           "moe_route", "moe_dispatch",
            "moe_dispatch_status", "moe_expert_ffn", "moe_expert_ffn_gate_up",
            "moe_expert_ffn_down", "moe_combine", "moe_combine_bwd",
            "moe_expert_ffn_bwd", "moe_route_bwd", "moe_dispatch_bwd", "moe_ep_recv_plan",
@@ -42,6 +43,7 @@ _P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_
 EXPORTED = {
     "moe_abi_version": (_I32, []),
     "moe_status_str": (ctypes.c_char_p, [_I32]),
+    "moe_workspace_size": (_SZ, [_I32, _I64, _I32, _I32, _P, _I64, _I64, _I64, _I32]),
     "moe_route": (_I32, [_P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P]),
     "moe_dispatch_workspace_size": (_SZ, [_I64, _I32, _I32, _P]),
     "moe_dispatch": (_I32, [_P, _P, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
@@ -139,6 +141,18 @@ def _stream(stream=None):
 
 def moe_abi_version() -> int:
     return int(load().moe_abi_version())
+
+
+MOE_OP_DISPATCH, MOE_OP_EXPERT_FFN, MOE_OP_EXPERT_FFN_BWD = 0, 1, 2
+
+
+def moe_workspace_size(op: int, *, T: int = 0, E: int = 0, k: int = 0,
+                       layout: Optional["Layout"] = None, rows: int = 0, d: int = 0, F: int = 0,
+                       dtype: torch.dtype = torch.bfloat16) -> int:
+    """Workspace bytes of one call of operation `op` (moe_workspace_size)."""
+    clay = layout._c() if layout else None
+    return int(load().moe_workspace_size(op, T, E, k, ctypes.byref(clay) if clay is not None else None,
+                                         rows, d, F, MOE_BF16 if dtype == torch.bfloat16 else MOE_F32))
 
 
 # ------------------------------------------------------------------ forward

@@ -16,3 +16,14 @@ extern "C" const char *moe_status_str(moe_status_t s) {
     default: return "unknown status";
     }
 }
+
+extern "C" size_t moe_workspace_size(moe_op_t op, int64_t T, int32_t E, int32_t k,
+                                     const moe_layout_t *layout, int64_t rows, int64_t d,
+                                     int64_t F, moe_dtype_t dtype) {
+    switch (op) {
+    case MOE_OP_DISPATCH: return moe_dispatch_workspace_size(T, E, k, layout);
+    case MOE_OP_EXPERT_FFN: return moe_expert_ffn_workspace_size(E, rows, d, F, dtype);
+    case MOE_OP_EXPERT_FFN_BWD: return moe_expert_ffn_bwd_workspace_size(E, rows, d, F, dtype);
+    default: return 0;
+    }
+}

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "moe.h"
 
 namespace moe {
@@ -21,6 +23,31 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+// One-time set-up per GPU (kernel attributes, device queries). The library's only
+// process-wide state: every device the process calls the library on runs `f` once,
+// with that device current, and its result is kept for that device. Thread-safe.
+constexpr int kMaxDevices = 64;
+struct PerDevice {
+    std::once_flag once[kMaxDevices];
+    int value[kMaxDevices] = {};
+};
+template <class F> int per_device(PerDevice &pd, F f) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return f();
+    std::call_once(pd.once[dev], [&] { pd.value[dev] = f(); });
+    return pd.value[dev];
+}
+
+// Raises a kernel's dynamic LDS limit on the current device (once per device).
+template <auto Kernel> bool lds_limit_once(int bytes) {
+    static PerDevice pd;
+    return per_device(pd, [bytes] {
+               return int(hipFuncSetAttribute(reinterpret_cast<const void *>(Kernel),
+                                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                                              bytes) == hipSuccess);
+           }) != 0;
+}
 
 inline moe_status_t launch_status() {
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;

@@ -24,6 +24,8 @@
 // Prefix sums in k_plan_scan are segmented scans built from wavefront shuffles.
 #include "common.h"
 
+#include <algorithm>
+
 namespace moe {
 namespace {
 
@@ -555,14 +557,24 @@ __global__ __launch_bounds__(256) void k_dispatch_bwd(const uint4 *__restrict__ 
     }
 }
 
-bool set_scan_lds_limit() {
-    static int ok = -1;
-    if (ok < 0)
-        ok = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_plan_scan),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 kScanLdsInts * int(sizeof(int))) == hipSuccess;
-    return ok == 1;
+// An empty batch (T = 0): every count and offset is zero, every row of the buffer is
+// unused, and the status flag is cleared, so a later consumer of the plan (combine,
+// the backward) reads a valid empty plan rather than whatever the buffers held.
+__global__ __launch_bounds__(256) void k_plan_empty(PlanGeom g, int *__restrict__ counts,
+                                                     int *__restrict__ expert_off,
+                                                     int *__restrict__ chunk_off,
+                                                     int *__restrict__ row_pair,
+                                                     int *__restrict__ flag) {
+    const int64_t tid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+    if (tid == 0) *flag = 0;
+    for (int64_t i = tid; i < int64_t(g.n_src) * g.E; i += stride) counts[i] = 0;
+    for (int64_t i = tid; i <= g.E; i += stride) expert_off[i] = 0;
+    for (int64_t i = tid; i < int64_t(g.n_dst) * (g.n_src + 1); i += stride) chunk_off[i] = 0;
+    for (int64_t i = tid; i < int64_t(g.n_dst) * g.cap; i += stride) row_pair[i] = -1;
 }
+
+bool set_scan_lds_limit() { return lds_limit_once<&k_plan_scan>(kScanLdsInts * int(sizeof(int))); }
 
 int copy_grid(int64_t T) { return int(std::min<int64_t>(cdiv(T, 4), 8192)); }
 
@@ -601,11 +613,27 @@ moe_status_t dispatch_impl(const void *x, const int32_t *topk_idx, int64_t T, in
     const int64_t need = int64_t(n_src) * g.Ts * std::min<int64_t>(k, g.epr);
     if (g.cap < need) return MOE_ERR_CAPACITY;
     if (int64_t(n_dst) * g.cap >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+    // the expert-major layout scans with k_plan_scan_em, which walks the plan blocks in
+    // batches and needs no LDS beyond its own; the rank-major scan keeps every block
+    // count, per-source count and chunk size of the plan in one workgroup's LDS
+    const bool expert_major = n_src == 1 && n_dst == 1;
     const size_t lds_scan = size_t(int64_t(g.B) * E + int64_t(n_src) * E + E + 1 +
                                    int64_t(n_dst) * (n_src + 1) + int64_t(n_src) * n_dst) *
                             sizeof(int);
-    if (lds_scan > size_t(kScanLdsInts) * sizeof(int)) return MOE_ERR_UNSUPPORTED;
-    if (T == 0) return MOE_OK;
+    if (!expert_major && lds_scan > size_t(kScanLdsInts) * sizeof(int)) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) {
+        // plan only: nothing to read, but the plan outputs describe an empty batch
+        if (!counts || !expert_off || !chunk_off || !ws || (g.cap > 0 && !row_pair))
+            return MOE_ERR_INVALID_ARG;
+        if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return MOE_ERR_ALIGN;
+        if (ws_bytes < ws_bytes_for(g)) return MOE_ERR_CAPACITY;
+        const int64_t n = std::max<int64_t>({int64_t(n_dst) * g.cap, int64_t(E) + 1,
+                                             int64_t(n_src) * E, int64_t(n_dst) * (n_src + 1)});
+        hipLaunchKernelGGL(k_plan_empty, dim3(unsigned(std::min<int64_t>(cdiv(n, 256), 1024))),
+                           dim3(256), 0, as_stream(stream), g, counts, expert_off, chunk_off,
+                           row_pair, reinterpret_cast<int *>(ws));
+        return launch_status();
+    }
     if (!topk_idx || !counts || !expert_off || !chunk_off || !pair_slot || !row_pair || !ws)
         return MOE_ERR_INVALID_ARG;
     if (!q8 && (x == nullptr) != (x_disp == nullptr)) return MOE_ERR_INVALID_ARG;
@@ -629,7 +657,7 @@ moe_status_t dispatch_impl(const void *x, const int32_t *topk_idx, int64_t T, in
 
     hipLaunchKernelGGL(k_plan_count, dim3(g.B), dim3(kPlanBlock), lds_mask, st, topk_idx, g,
                        blk_counts, blk_flags);
-    if (n_src == 1 && n_dst == 1 && g.B <= 256)
+    if (expert_major)
         hipLaunchKernelGGL(k_plan_scan_em, dim3(1), dim3(kScanThreads), 0, st, blk_counts,
                            blk_flags, g, counts, expert_off, chunk_off, blk_base, flag);
     else

@@ -493,17 +493,9 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float *__restrict__ A,
 }
 
 bool set_lds_limits() {
-    static bool ok = false;
-    static std::once_flag once;
-    std::call_once(once, [] {
-        ok = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_bf16<EPI_SWIGLU, false>),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, kLdsFwd) == hipSuccess &&
-             hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_bf16<EPI_SWIGLU, true>),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, kLdsFwd) == hipSuccess &&
-             hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_bf16<EPI_PLAIN, true>),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, kLdsFwd) == hipSuccess;
-    });
-    return ok;
+    return lds_limit_once<&k_gemm_bf16<EPI_SWIGLU, false>>(kLdsFwd) &&
+           lds_limit_once<&k_gemm_bf16<EPI_SWIGLU, true>>(kLdsFwd) &&
+           lds_limit_once<&k_gemm_bf16<EPI_PLAIN, true>>(kLdsFwd);
 }
 
 // Workspace of the composite call: the activation a [rows, F] in dtype.

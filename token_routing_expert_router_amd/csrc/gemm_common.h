@@ -87,18 +87,16 @@ __device__ __forceinline__ ItemCoord decode_item(int item, const int *tile_off, 
     return {lo, rem / mc, rem % mc};
 }
 
+// Compute units of the current device (queried once per device).
 inline int num_cus() {
-    static int n = 0;
-    static std::once_flag once;
-    std::call_once(once, [] {
+    static PerDevice pd;
+    return per_device(pd, [] {
         int dev = 0, v = 0;
         if (hipGetDevice(&dev) == hipSuccess &&
             hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            n = v;
-        else
-            n = 256;
+            return v;
+        return 256;
     });
-    return n;
 }
 
 }  // namespace moe

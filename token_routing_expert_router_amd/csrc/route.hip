@@ -419,13 +419,7 @@ moe_status_t launch_route_mfma_cfg(const uint16_t *x, const uint16_t *w, int T, 
     if (int64_t(E) * d * 2 > 0x7fffffff || d > (1 << 26)) return MOE_ERR_UNSUPPORTED;
     const size_t stage = size_t(kRouteTT + ep) * (BK + 4) * sizeof(float);
     const size_t lds = std::max(2 * stage, size_t(kRouteTT) * (ep + 1) * sizeof(float));
-    static std::once_flag once;
-    static bool lds_ok = false;
-    std::call_once(once, [] {
-        lds_ok = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_router_mfma<NCH, NV, BK, CPTW>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess;
-    });
-    if (!lds_ok) return MOE_ERR_HIP;
+    if (!lds_limit_once<&k_router_mfma<NCH, NV, BK, CPTW>>(160 * 1024)) return MOE_ERR_HIP;
     hipLaunchKernelGGL((k_router_mfma<NCH, NV, BK, CPTW>), dim3(unsigned(cdiv(T, kRouteTT))),
                        dim3(64 * nw), lds, st, x, w, T, d, E, k, full, logits, idx, gw);
     return launch_status();
@@ -618,13 +612,7 @@ moe_status_t launch_route16_cfg(const uint16_t *x, const uint16_t *w, int T, int
     const size_t stage = size_t(TT + EP) * (BK + 4) * sizeof(float);
     const size_t lds = std::max(2 * stage, size_t(TT) * (EP + 1) * sizeof(float));
     if (lds > 160 * 1024) return MOE_ERR_UNSUPPORTED;
-    static std::once_flag once;
-    static bool lds_ok = false;
-    std::call_once(once, [] {
-        lds_ok = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_router_mfma16<TG, EG, NC, BK, NLW>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess;
-    });
-    if (!lds_ok) return MOE_ERR_HIP;
+    if (!lds_limit_once<&k_router_mfma16<TG, EG, NC, BK, NLW>>(160 * 1024)) return MOE_ERR_HIP;
     hipLaunchKernelGGL((k_router_mfma16<TG, EG, NC, BK, NLW>), dim3(unsigned(cdiv(T, TT))),
                        dim3(kWave * nw), lds, st, x, w, T, d, E, k, full, logits, idx, gw);
     return launch_status();
@@ -645,7 +633,10 @@ moe_status_t launch_route_mfma(const void *x, const void *w, int T, int d, int E
     if (eg <= 2) return launch_route16_cfg<2, 2, 1, 32, 2>(xb, wb, T, d, E, k, full, logits, idx, gw, st, 8);
     if (eg <= 4) return launch_route16_cfg<2, 4, 2, 32, 4>(xb, wb, T, d, E, k, full, logits, idx, gw, st, 8);
     if (eg <= 6) return launch_route16_cfg<2, 6, 3, 32, 6>(xb, wb, T, d, E, k, full, logits, idx, gw, st, 8);
-    return launch_route16_cfg<2, 8, 4, 32, 8>(xb, wb, T, d, E, k, full, logits, idx, gw, st, 8);
+    if (eg <= 8) return launch_route16_cfg<2, 8, 4, 32, 8>(xb, wb, T, d, E, k, full, logits, idx, gw, st, 8);
+    // up to 1024 experts: 16 tokens per workgroup and 8-deep stages keep two float32
+    // stages of 16 + 1024 rows (100 KiB) in LDS; four waves of four chains each
+    return launch_route16_cfg<1, 16, 4, 8, 4>(xb, wb, T, d, E, k, full, logits, idx, gw, st, 8);
 }
 
 template <int DT, int TM>
@@ -689,7 +680,10 @@ extern "C" moe_status_t moe_route(const void *x, const void *w_router, int64_t T
         return MOE_ERR_INVALID_ARG;
     if (T < 0 || d <= 0 || E <= 0 || k <= 0) return MOE_ERR_INVALID_ARG;
     if (k > E) return MOE_ERR_SHAPE;
-    if (k > 32 || E > 512 || T > (int64_t(1) << 31) / 64 || d > (int64_t(1) << 30))
+    // bf16 takes up to 1024 experts; the float32 kernel keeps its logits tile and the
+    // expert rows of a stage in static LDS, which holds 512
+    if (k > 32 || E > (dtype == MOE_BF16 ? 1024 : 512) || T > (int64_t(1) << 31) / 64 ||
+        d > (int64_t(1) << 30))
         return MOE_ERR_UNSUPPORTED;
     if (T == 0) return MOE_OK;
     if (!x || !w_router || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;

@@ -7,6 +7,8 @@
 // tokens, in one fixed order (eight interleaved float32 partial sums, see below).
 #include "common.h"
 
+#include <algorithm>
+
 namespace moe {
 namespace {
 
@@ -19,6 +21,13 @@ __global__ void k_route_bwd_sel(const float *__restrict__ g, const float *__rest
     float s = 0.0f;
     for (int j = 0; j < k; ++j) s = __builtin_fmaf(gt[j], dgt[j], s);
     for (int j = 0; j < k; ++j) dl[size_t(t) * k + j] = gt[j] * (dgt[j] - s);
+}
+
+// dw = 0 (the router gradient of an empty batch: there is no plan to read).
+__global__ __launch_bounds__(256) void k_zero_f32(float4 *__restrict__ p, int64_t n4) {
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n4;
+         i += int64_t(gridDim.x) * blockDim.x)
+        p[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 }
 
 // One workgroup per (expert, 32 16-byte chunks of the row). Its 256 threads are 8 row
@@ -101,15 +110,23 @@ extern "C" moe_status_t moe_route_bwd(const void *x, const int32_t *topk_idx, co
     if (!valid_dtype(dtype) || T < 0 || d <= 0 || E <= 0 || k <= 0) return MOE_ERR_INVALID_ARG;
     if (k > E) return MOE_ERR_SHAPE;
     if (E > 65535 || T * k >= (int64_t(1) << 31) || d > (int64_t(1) << 24)) return MOE_ERR_UNSUPPORTED;
+    const int64_t rowb = d * elt_size(dtype);
+    const hipStream_t st = as_stream(stream);
+    if (T == 0) {
+        // an empty batch: dw_router = 0, and nothing of the plan or x is read
+        if (!dw_router) return MOE_ERR_INVALID_ARG;
+        if (rowb % 16 != 0 || !aligned16(dw_router)) return MOE_ERR_ALIGN;
+        const int64_t n4 = int64_t(E) * d / 4;      // d * 4 bytes % 16 == 0 by the check above
+        hipLaunchKernelGGL(k_zero_f32, dim3(unsigned(std::min<int64_t>(cdiv(n4, 256), 4096))),
+                           dim3(256), 0, st, reinterpret_cast<float4 *>(dw_router), n4);
+        return launch_status();
+    }
     if (!x || !topk_idx || !topk_w || !dtopk_w || !expert_off || !row_pair || !dlogits_sel ||
         !dw_router)
         return MOE_ERR_INVALID_ARG;
-    const int64_t rowb = d * elt_size(dtype);
     if (rowb % 16 != 0 || !aligned16(x) || !aligned16(dw_router)) return MOE_ERR_ALIGN;
-    const hipStream_t st = as_stream(stream);
-    if (T > 0)
-        hipLaunchKernelGGL(k_route_bwd_sel, dim3(unsigned(cdiv(T, 256))), dim3(256), 0, st, topk_w,
-                           dtopk_w, int(T), k, dlogits_sel);
+    hipLaunchKernelGGL(k_route_bwd_sel, dim3(unsigned(cdiv(T, 256))), dim3(256), 0, st, topk_w,
+                       dtopk_w, int(T), k, dlogits_sel);
     const int rc = int(rowb / 16);
     const dim3 grid(unsigned(E), unsigned(cdiv(rc, kRbChunks)));
     if (dtype == MOE_BF16)
