@@ -162,6 +162,24 @@ moe_status_t moe_dispatch(const void *x, const int32_t *topk_idx, int64_t T, int
                           int32_t *counts, int32_t *expert_off, int32_t *chunk_off,
                           int32_t *pair_slot, int32_t *row_pair, void *x_disp, void *ws,
                           size_t ws_bytes, void *stream);
+/* moe_dispatch_noalloc: moe_dispatch for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same plan and copy, bit for bit, with the workspace taken from a fixed array of
+ * 4 MiB per GPU inside the library (a __device__ array, resident from the library's
+ * load until the process ends) instead of `ws`. The call itself allocates nothing.
+ * Limit: the plan's workspace (moe_dispatch_workspace_size of the same sizes) must fit
+ * 4 MiB, e.g. T <= 349,184 tokens at E = 384 or T <= 130,816 at E = 1024 in the
+ * expert-major layout; larger plans return MOE_ERR_CAPACITY before anything runs.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU (two
+ * streams, two host threads) race and must be serialised by the caller. Nothing in
+ * the array needs clearing between calls. The device status flag lives in the array
+ * and moe_dispatch_status cannot read it; a skipped pair shows as pair_slot = -1 and
+ * an over-full destination as chunk_off[r][n_src] > cap_rows_per_dst. */
+moe_status_t moe_dispatch_noalloc(const void *x, const int32_t *topk_idx, int64_t T, int64_t d,
+                                  int32_t E, int32_t k, moe_dtype_t dtype,
+                                  const moe_layout_t *layout, int32_t *counts,
+                                  int32_t *expert_off, int32_t *chunk_off, int32_t *pair_slot,
+                                  int32_t *row_pair, void *x_disp, void *stream);
 /* Waits for `stream`, then returns MOE_OK, MOE_ERR_BAD_INDEX or MOE_ERR_CAPACITY
  * from the flag the last moe_dispatch on `ws` raised. */
 moe_status_t moe_dispatch_status(const void *ws, void *stream);

@@ -225,3 +225,13 @@ def test_route_accepts_1024_experts_in_bf16(lib):
     assert r(FAKE, FAKE, 10, 64, 1024, 8, BF16, 0, None, None, FAKE, None) == INVALID
     assert r(FAKE, FAKE, 10, 64, 1024, 8, F32, 0, None, None, FAKE, None) == UNSUPPORTED
     assert r(FAKE, FAKE, 10, 64, 1025, 8, BF16, 0, None, None, FAKE, None) == UNSUPPORTED
+
+
+def test_noalloc_dispatch_rejects_plans_past_its_array(lib):
+    """The allocation-free dispatch refuses, before any HIP call, a plan whose workspace
+    exceeds its fixed 4 MiB array."""
+    n = lib.moe_dispatch_noalloc
+    T, E, k = 200_000, 1024, 8
+    assert lib.moe_dispatch_workspace_size(T, E, k, None) > 4 << 20
+    assert n(FAKE, FAKE, T, 64, E, k, BF16, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == CAPACITY
+    assert n(FAKE, FAKE, 10, 64, 8, 9, BF16, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == SHAPE

@@ -19,7 +19,7 @@ import torch
 
 __all__ = ["MoEError", "load", "library_path", "moe_abi_version", "moe_workspace_size",
            "moe_route", "moe_dispatch",
-           "moe_dispatch_status", "moe_expert_ffn", "moe_expert_ffn_gate_up",
+           "moe_dispatch_status", "moe_dispatch_noalloc", "moe_expert_ffn", "moe_expert_ffn_gate_up",
            "moe_expert_ffn_down", "moe_combine", "moe_combine_bwd",
            "moe_expert_ffn_bwd", "moe_route_bwd", "moe_dispatch_bwd", "moe_ep_recv_plan",
            "moe_ep_recv_gather", "moe_ep_recv_scatter", "moe_dispatch_fp8",
@@ -49,6 +49,8 @@ EXPORTED = {
     "moe_dispatch": (_I32, [_P, _P, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
                             _P, _SZ, _P]),
     "moe_dispatch_status": (_I32, [_P, _P]),
+    "moe_dispatch_noalloc": (_I32, [_P, _P, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P,
+                                    _P, _P]),
     "moe_expert_ffn_workspace_size": (_SZ, [_I32, _I64, _I64, _I64, _I32]),
     "moe_expert_ffn": (_I32, [_P, _P, _P, _P, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _SZ,
                               _P]),
@@ -207,6 +209,34 @@ def moe_dispatch(x, topk_idx, E: int, *, layout: Optional[Layout] = None, d: Opt
         _ptr(x), _ptr(topk_idx), T, d if d is not None else 8, E, k, dt, lay_ptr,
         _ptr(o["counts"]), _ptr(o["expert_off"]), _ptr(o["chunk_off"]), _ptr(o["pair_slot"]),
         _ptr(o["row_pair"]), _ptr(o["x_disp"]), _ptr(o["ws"]), o["ws"].numel(), _stream(stream)))
+    return o
+
+
+def moe_dispatch_noalloc(x, topk_idx, E: int, *, layout: Optional[Layout] = None,
+                         out: Optional[dict] = None, stream=None):
+    """moe_dispatch with its workspace in the library's fixed per-GPU array (no ws).
+    Returns the plan dict (counts, expert_off, chunk_off, pair_slot, row_pair, x_disp);
+    outputs not passed in `out` are allocated here, by torch, before the call."""
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    d = x.shape[1]
+    n_src = layout.n_src if layout else 1
+    n_dst = layout.n_dst if layout else 1
+    cap = layout.cap if layout else T * k
+    clay = layout._c() if layout else None
+    o = dict(out or {})
+    for name, shape in (("counts", (n_src, E)), ("expert_off", (E + 1,)),
+                        ("chunk_off", (n_dst, n_src + 1)), ("pair_slot", (T, k)),
+                        ("row_pair", (n_dst * cap,))):
+        if o.get(name) is None:
+            o[name] = torch.empty(shape, dtype=torch.int32, device=dev)
+    if o.get("x_disp") is None:
+        o["x_disp"] = torch.empty((n_dst * cap, d), dtype=x.dtype, device=dev)
+    _check("moe_dispatch_noalloc", load().moe_dispatch_noalloc(
+        _ptr(x), _ptr(topk_idx), T, d, E, k, _dt(x),
+        ctypes.byref(clay) if clay is not None else None, _ptr(o["counts"]),
+        _ptr(o["expert_off"]), _ptr(o["chunk_off"]), _ptr(o["pair_slot"]), _ptr(o["row_pair"]),
+        _ptr(o["x_disp"]), _stream(stream)))
     return o
 
 

@@ -28,11 +28,11 @@ inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s);
 // process-wide state: every device the process calls the library on runs `f` once,
 // with that device current, and its result is kept for that device. Thread-safe.
 constexpr int kMaxDevices = 64;
-struct PerDevice {
+template <class T = int> struct PerDevice {
     std::once_flag once[kMaxDevices];
-    int value[kMaxDevices] = {};
+    T value[kMaxDevices] = {};
 };
-template <class F> int per_device(PerDevice &pd, F f) {
+template <class T, class F> T per_device(PerDevice<T> &pd, F f) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return f();
     std::call_once(pd.once[dev], [&] { pd.value[dev] = f(); });
@@ -41,7 +41,7 @@ template <class F> int per_device(PerDevice &pd, F f) {
 
 // Raises a kernel's dynamic LDS limit on the current device (once per device).
 template <auto Kernel> bool lds_limit_once(int bytes) {
-    static PerDevice pd;
+    static PerDevice<int> pd;
     return per_device(pd, [bytes] {
                return int(hipFuncSetAttribute(reinterpret_cast<const void *>(Kernel),
                                               hipFuncAttributeMaxDynamicSharedMemorySize,

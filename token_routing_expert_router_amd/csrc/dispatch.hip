@@ -576,6 +576,21 @@ __global__ __launch_bounds__(256) void k_plan_empty(PlanGeom g, int *__restrict_
 
 bool set_scan_lds_limit() { return lds_limit_once<&k_plan_scan>(kScanLdsInts * int(sizeof(int))); }
 
+// The allocation-free dispatch's workspace: one fixed array per GPU, held until the
+// process ends. Its name is a host-side stand-in; kernels get the device address that
+// hipGetSymbolAddress returns for the current device (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+void *scratch_ptr() {
+    static PerDevice<void *> pd;
+    return per_device(pd, []() -> void * {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        return ptr;
+    });
+}
+
 int copy_grid(int64_t T) { return int(std::min<int64_t>(cdiv(T, 4), 8192)); }
 
 }  // namespace
@@ -594,11 +609,13 @@ namespace moe {
 namespace {
 
 // The plan, then either the row copy (x_disp) or the fp8 payload (q_disp, q_scale).
+// noalloc: the workspace is this device's scratch array (ws and ws_bytes are ignored).
 moe_status_t dispatch_impl(const void *x, const int32_t *topk_idx, int64_t T, int64_t d,
                            int32_t E, int32_t k, moe_dtype_t dtype, const moe_layout_t *layout,
                            int32_t *counts, int32_t *expert_off, int32_t *chunk_off,
                            int32_t *pair_slot, int32_t *row_pair, void *x_disp, uint8_t *q_disp,
-                           float *q_scale, void *ws, size_t ws_bytes, void *stream) {
+                           float *q_scale, void *ws, size_t ws_bytes, void *stream,
+                           bool noalloc = false) {
     const bool q8 = q_disp != nullptr || q_scale != nullptr;
     if (!valid_dtype(dtype) || T < 0 || d <= 0 || E <= 0 || k <= 0) return MOE_ERR_INVALID_ARG;
     if (k > E) return MOE_ERR_SHAPE;
@@ -621,6 +638,13 @@ moe_status_t dispatch_impl(const void *x, const int32_t *topk_idx, int64_t T, in
                                    int64_t(n_dst) * (n_src + 1) + int64_t(n_src) * n_dst) *
                             sizeof(int);
     if (!expert_major && lds_scan > size_t(kScanLdsInts) * sizeof(int)) return MOE_ERR_UNSUPPORTED;
+    if (noalloc) {
+        // the plan's workspace must fit the fixed array; nothing is allocated instead
+        if (ws_bytes_for(g) > kNoAllocScratchBytes) return MOE_ERR_CAPACITY;
+        ws = scratch_ptr();
+        if (ws == nullptr) return MOE_ERR_HIP;
+        ws_bytes = kNoAllocScratchBytes;
+    }
     if (T == 0) {
         // plan only: nothing to read, but the plan outputs describe an empty batch
         if (!counts || !expert_off || !chunk_off || !ws || (g.cap > 0 && !row_pair))
@@ -687,6 +711,17 @@ extern "C" moe_status_t moe_dispatch(const void *x, const int32_t *topk_idx, int
                                      void *stream) {
     return dispatch_impl(x, topk_idx, T, d, E, k, dtype, layout, counts, expert_off, chunk_off,
                          pair_slot, row_pair, x_disp, nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+extern "C" moe_status_t moe_dispatch_noalloc(const void *x, const int32_t *topk_idx, int64_t T,
+                                             int64_t d, int32_t E, int32_t k, moe_dtype_t dtype,
+                                             const moe_layout_t *layout, int32_t *counts,
+                                             int32_t *expert_off, int32_t *chunk_off,
+                                             int32_t *pair_slot, int32_t *row_pair, void *x_disp,
+                                             void *stream) {
+    return dispatch_impl(x, topk_idx, T, d, E, k, dtype, layout, counts, expert_off, chunk_off,
+                         pair_slot, row_pair, x_disp, nullptr, nullptr, nullptr, 0, stream,
+                         /*noalloc=*/true);
 }
 
 extern "C" moe_status_t moe_dispatch_fp8(const void *x, const int32_t *topk_idx, int64_t T,

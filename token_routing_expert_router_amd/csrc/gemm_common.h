@@ -89,7 +89,7 @@ __device__ __forceinline__ ItemCoord decode_item(int item, const int *tile_off, 
 
 // Compute units of the current device (queried once per device).
 inline int num_cus() {
-    static PerDevice pd;
+    static PerDevice<int> pd;
     return per_device(pd, [] {
         int dev = 0, v = 0;
         if (hipGetDevice(&dev) == hipSuccess &&
