@@ -406,6 +406,27 @@ def overlap_bench(torch, moe, wl, dev, steps, warmup):
     res["whole_batch_us"] = run(lambda: moe.forward(x, wr, w13, w2, wl.k))
     res["two_microbatches_two_streams_us"] = run(
         lambda: moe.forward_microbatched(x, wr, w13, w2, wl.k, 2, streams=[main, side], y=y_mb))
+    # the rank-major path in its send and receive halves (8 destination regions of 8
+    # experts): destinations' receive paths on one stream, then alternating on two
+    # (micro-batches by expert group: every weight read once); and the same with the
+    # shared expert on the side stream during the send half
+    nd = 8
+    o_ep = moe.forward_ep_split(x, wr, w13, w2, wl.k, nd)
+    o_eps = moe.forward_ep_split(x, wr, w13, w2, wl.k, nd, streams=[main, side])
+    o_epx = moe.forward_ep_split(x, wr, w13, w2, wl.k, nd, w13_shared=w13s, w2_shared=w2s)
+    o_epxs = moe.forward_ep_split(x, wr, w13, w2, wl.k, nd, w13_shared=w13s, w2_shared=w2s,
+                                  streams=[main, side])
+    res["ep_split_destinations"] = nd
+    res["ep_split_one_stream_us"] = run(lambda: moe.forward_ep_split(x, wr, w13, w2, wl.k, nd,
+                                                                     out=o_ep))
+    res["ep_split_two_streams_us"] = run(lambda: moe.forward_ep_split(
+        x, wr, w13, w2, wl.k, nd, streams=[main, side], out=o_eps))
+    res["ep_split_shared_one_stream_us"] = run(lambda: moe.forward_ep_split(
+        x, wr, w13, w2, wl.k, nd, w13_shared=w13s, w2_shared=w2s, out=o_epx))
+    res["ep_split_shared_two_streams_us"] = run(lambda: moe.forward_ep_split(
+        x, wr, w13, w2, wl.k, nd, w13_shared=w13s, w2_shared=w2s, streams=[main, side],
+        out=o_epxs))
+    del o_ep, o_eps, o_epx, o_epxs
     del inp, o_serial, o_over
     return res
 

@@ -72,3 +72,42 @@ def test_microbatched_equals_whole_batch(gpu_lib, n_micro):
     eerr = oracle.elementwise_rel_err(_np(y_mb), ref["y"])
     _say(f"  err {err:.2e} (elementwise {eerr:.2e})")
     assert err <= BF16_TOL and eerr <= BF16_TOL
+
+
+@pytest.mark.parametrize("T,d,E,k,F,n_dst", [(300, 256, 16, 4, 192, 4), (4096, 2048, 64, 6, 1408, 8)])
+def test_ep_split_send_receive(gpu_lib, T, d, E, k, F, n_dst):
+    """The send half (route + rank-major dispatch into n_dst regions) and the receive half
+    (per destination: reorder, local grouped GEMM, scatter back), on one stream and with
+    destinations alternating between two streams, with and without the shared expert on
+    the side stream: equal to the expert-major forward bit for bit (one source), the plan
+    equal to the oracle's, and y within the bf16 bar of the oracle's layer."""
+    moe = gpu_lib
+    wl = moe_synth.small_workload(moe_synth.WORKLOADS["mid_bf16"], T=T, d=d, E=E, k=k, F=F)
+    _say(f"ep split {wl} n_dst={n_dst}")
+    inp = moe_synth.layer_inputs(wl, device="cuda")
+    x, wr, w13, w2 = inp["x"], inp["w_router"], inp["w13"], inp["w2"]
+    w13s, w2s = _shared_weights(wl, "cuda")
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    o1 = moe.forward_ep_split(x, wr, w13, w2, k, n_dst)
+    o2 = moe.forward_ep_split(x, wr, w13, w2, k, n_dst, streams=[main, side])
+    o3 = moe.forward_ep_split(x, wr, w13, w2, k, n_dst, w13_shared=w13s, w2_shared=w2s,
+                              streams=[main, side])
+    y0 = moe.forward(x, wr, w13, w2, k)["y"]
+    ys = moe.forward_shared(x, wr, w13, w2, w13s, w2s, k)["y"]
+    torch.cuda.synchronize()
+    assert torch.equal(o1["y"].view(torch.int16), y0.view(torch.int16))
+    assert torch.equal(o2["y"].view(torch.int16), y0.view(torch.int16))
+    assert torch.equal(o3["y"].view(torch.int16), ys.view(torch.int16))
+    host = {n: t.cpu() for n, t in inp.items()}
+    ref = oracle.forward(host["x"], host["w_router"], host["w13"], host["w2"], k)
+    cap = T * max(k, E // n_dst)
+    ref_plan = oracle.plan(ref["idx"], E, 1, n_dst, cap)
+    for key in ("counts", "chunk_off", "pair_slot", "row_pair"):
+        got = o2["plan"][key].cpu().numpy().reshape(ref_plan[key].shape)
+        assert np.array_equal(got, ref_plan[key]), key
+    err = oracle.normwise_rel_err(_np(o2["y"]), ref["y"])
+    eerr = oracle.elementwise_rel_err(_np(o2["y"]), ref["y"])
+    ref_s = ref["y"] + oracle.swiglu_expert(_np(x), w13s.cpu(), w2s.cpu())
+    err_s = oracle.normwise_rel_err(_np(o3["y"]), ref_s)
+    _say(f"  err {err:.2e} (elementwise {eerr:.2e}); with shared expert {err_s:.2e}")
+    assert err <= BF16_TOL and eerr <= BF16_TOL and err_s <= BF16_TOL

@@ -24,7 +24,7 @@ __all__ = ["MoEError", "load", "library_path", "moe_abi_version", "moe_workspace
            "moe_expert_ffn_bwd", "moe_route_bwd", "moe_dispatch_bwd", "moe_ep_recv_plan",
            "moe_ep_recv_gather", "moe_ep_recv_scatter", "moe_dispatch_fp8",
            "moe_ep_recv_gather_fp8", "moe_combine_partial", "moe_combine_partials", "moe_combine_add",
-           "forward_shared", "forward_microbatched", "Layout", "forward",
+           "forward_shared", "forward_microbatched", "forward_ep_split", "Layout", "forward",
            "backward",
            "EXPORTED"]
 
@@ -540,6 +540,96 @@ def forward_microbatched(x, w_router, w13, w2, k: int, n_micro: int = 2, *, stre
         if s is not main:
             main.wait_stream(s)
     return y
+
+
+def forward_ep_split(x, w_router, w13, w2, k: int, n_dst: int, *, w13_shared=None,
+                     w2_shared=None, streams=None, out: Optional[dict] = None):
+    """The layer on the rank-major (emulated expert-parallel) path, in its two halves.
+
+    send:    moe_route, then moe_dispatch into n_dst destination regions of
+             cap = T * max(k, E/n_dst) rows each (one contiguous chunk per sender);
+    receive: for every destination r, moe_ep_recv_plan + moe_ep_recv_gather into its
+             local expert-major order, its grouped GEMM over its E/n_dst experts
+             (moe_expert_ffn_gate_up / _down with those experts' weights), and
+             moe_ep_recv_scatter of the outputs back into its region;
+    combine: moe_combine_add over the whole rank-major buffer, starting from the shared
+             expert's output (a SwiGLU on every token, E = 1) when w13_shared is given.
+
+    ([EFA] Dispatch and combine: the sender and receiver halves are separate kernels, so
+    that the GPU can do other work, such as a shared expert, while the transfer is in
+    flight.) streams = [main, side]: the shared expert runs on side while main runs the
+    send half, and the destinations' receive paths alternate between main and side, so
+    one destination's memory-bound gather and scatter overlap another's GEMM; each
+    expert's weights are still read once. With streams None everything runs on the
+    current stream in the same order. With one source the local order of a destination
+    is the expert-major order restricted to its experts, so y equals forward()'s y (plus
+    the shared expert's output) bit for bit."""
+    T, d = x.shape
+    E = w_router.shape[0]
+    F = w13.shape[1] // 2
+    assert E % n_dst == 0
+    epr = E // n_dst
+    cap = T * max(k, epr)
+    main = torch.cuda.current_stream()
+    streams = list(streams) if streams else [main]
+    side = streams[1] if len(streams) > 1 else main
+    o = dict(out or {})
+    dev = x.device
+    for s in streams:
+        if s is not main:
+            s.wait_stream(main)
+    shared = None
+    if w13_shared is not None:
+        if o.get("shared_off") is None:
+            o["shared_off"] = torch.tensor([0, T], dtype=torch.int32, device=dev)
+        with torch.cuda.stream(side):
+            shared = moe_expert_ffn(x, o["shared_off"], w13_shared.unsqueeze(0),
+                                    w2_shared.unsqueeze(0), y_disp=o.get("shared"), stream=side)
+    # send half
+    idx, gates, _ = moe_route(x, w_router, k, topk_idx=o.get("topk_idx"), topk_w=o.get("topk_w"),
+                              stream=main)
+    lay = Layout(1, n_dst, cap)
+    plan = moe_dispatch(x, idx, E, layout=lay, out=o.get("plan"), stream=main)
+    sent = torch.cuda.Event()
+    sent.record(main)
+    if o.get("y_disp") is None:
+        o["y_disp"] = torch.empty((n_dst * cap, d), dtype=x.dtype, device=dev)
+    y_disp = o["y_disp"]
+    # receive half, destination r on streams[r % len(streams)]; one set of local buffers
+    # per stream (work on one stream runs in order)
+    bufs = o.setdefault("recv_bufs", {})
+    for r in range(n_dst):
+        s = streams[r % len(streams)]
+        if r < len(streams):
+            s.wait_event(sent)
+        b = bufs.get(r % len(streams))
+        if b is None:
+            b = dict(x_local=torch.empty((cap, d), dtype=x.dtype, device=dev),
+                     act=torch.empty((cap, F), dtype=x.dtype, device=dev),
+                     y_local=torch.empty((cap, d), dtype=x.dtype, device=dev),
+                     local_off=torch.empty(epr + 1, dtype=torch.int32, device=dev),
+                     row_src=torch.empty(cap, dtype=torch.int32, device=dev))
+            bufs[r % len(streams)] = b
+        with torch.cuda.stream(s):
+            region = plan["x_disp"][r * cap:(r + 1) * cap]
+            moe_ep_recv_plan(plan["counts"], plan["chunk_off"], r, cap, local_off=b["local_off"],
+                             row_src=b["row_src"], stream=s)
+            moe_ep_recv_gather(region, b["row_src"], x_local=b["x_local"], stream=s)
+            moe_expert_ffn_gate_up(b["x_local"], b["local_off"], w13[r * epr:(r + 1) * epr],
+                                   act=b["act"], stream=s)
+            moe_expert_ffn_down(b["act"], b["local_off"], w2[r * epr:(r + 1) * epr],
+                                y_disp=b["y_local"], stream=s)
+            moe_ep_recv_scatter(b["y_local"], b["row_src"], y_disp[r * cap:(r + 1) * cap],
+                                stream=s)
+    for s in streams:
+        if s is not main:
+            main.wait_stream(s)
+    if shared is not None:
+        y = moe_combine_add(y_disp, plan["pair_slot"], gates, shared, y=o.get("y"), stream=main)
+    else:
+        y = moe_combine(y_disp, plan["pair_slot"], gates, y=o.get("y"), stream=main)
+    o.update(topk_idx=idx, topk_w=gates, plan=plan, y_disp=y_disp, shared=shared, y=y)
+    return o
 
 
 # ------------------------------------------------------------ whole layer
