@@ -168,7 +168,7 @@ moe_status_t moe_dispatch(const void *x, const int32_t *topk_idx, int64_t T, int
  * 4 MiB per GPU inside the library (a __device__ array, resident from the library's
  * load until the process ends) instead of `ws`. The call itself allocates nothing.
  * Limit: the plan's workspace (moe_dispatch_workspace_size of the same sizes) must fit
- * 4 MiB, e.g. T <= 349,184 tokens at E = 384 or T <= 130,816 at E = 1024 in the
+ * 4 MiB, e.g. T <= 209,408 tokens at E = 384 or T <= 104,704 at E = 1024 in the
  * expert-major layout; larger plans return MOE_ERR_CAPACITY before anything runs.
  * Every call on one GPU shares that GPU's array: calls that overlap on one GPU (two
  * streams, two host threads) race and must be serialised by the caller. Nothing in

@@ -49,6 +49,26 @@ template <auto Kernel> bool lds_limit_once(int bytes) {
            }) != 0;
 }
 
+// Division by a divisor fixed at launch, as a multiply and a shift (there is no integer
+// divide instruction; a runtime division costs dozens of instructions). For d >= 1 and
+// dividends n < 2^31: with p = ceil(log2 d) and m = ceil(2^(31+p) / d) (< 2^32),
+// n / d = (n * m) >> (31 + p) exactly, since n * m / 2^(31+p) exceeds n / d by less than
+// n / 2^(31+p) < 1 / d.
+struct FastDiv {
+    uint32_t d, m, k;
+    FastDiv() = default;
+    explicit FastDiv(uint32_t dv) : d(dv) {
+        uint32_t p = 0;
+        while ((uint64_t(1) << p) < dv) ++p;
+        k = 31 + p;
+        m = uint32_t(((uint64_t(1) << k) + dv - 1) / dv);
+    }
+    __device__ __forceinline__ int div(int n) const {   // 0 <= n < 2^31
+        return int((uint64_t(uint32_t(n)) * m) >> k);
+    }
+    __device__ __forceinline__ int64_t div64(int64_t n) const { return div(int(n)); }
+};
+
 inline moe_status_t launch_status() {
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

@@ -12,15 +12,16 @@
 //   k_plan_count  one workgroup per 256-token block of one source: every pair sets
 //                 bit (t mod 256) of its expert's 256-bit mask in LDS (atomic OR,
 //                 whose result does not depend on the order); popcounts are the
-//                 block's per-expert counts.
+//                 block's per-expert counts, and a pair's rank inside its expert is the
+//                 popcount of the mask bits below its token, so tokens keep their order
+//                 inside every expert. The ranks (< 256) go to the workspace as bytes.
 //   k_plan_scan   one workgroup: per-source counts, expert offsets, chunk offsets
 //                 per destination, and the first row of every (block, expert);
 //                 k_plan_scan_em is the short form for the expert-major layout.
-//   k_plan_slots_copy  rebuilds the masks; a pair's rank inside its expert is the
-//                 popcount of the mask bits below its token, so tokens keep their
-//                 order inside every expert; marks unused rows with -1; then copies:
-//                 one wavefront per token reads the row once with 16-byte loads and
-//                 writes it to each of its k rows (1 KiB per wavefront instruction).
+//   k_plan_copy   one wavefront per token: its k slots (first row of its block and
+//                 expert + its rank), the unused-row marks, then the row copy: the row
+//                 is read once with 16-byte loads and written to each of its k rows
+//                 (1 KiB per wavefront instruction).
 // Prefix sums in k_plan_scan are segmented scans built from wavefront shuffles.
 #include "common.h"
 
@@ -37,6 +38,11 @@ constexpr int kScanLdsInts = 32768;             // 128 KiB of LDS for the scan
 struct PlanGeom {
     int T, k, E, n_src, n_dst, Ts, bps, B, epr;
     int64_t cap;
+    FastDiv dE, dbps, depr, dTs, dcap;   // the same divisors, as multiply-shifts
+    // rank-major layout with one plan block per source and at most 64 experts per
+    // destination: the count kernel also takes each source's chunk sizes and the offset
+    // of every expert inside its chunk, and the scan only joins the sources
+    bool rm1;
 };
 
 PlanGeom make_geom(int64_t T, int32_t E, int32_t k, const moe_layout_t *lay) {
@@ -51,51 +57,126 @@ PlanGeom make_geom(int64_t T, int32_t E, int32_t k, const moe_layout_t *lay) {
     g.bps = int(cdiv(g.Ts, kPlanBlock));
     g.B = g.n_src * g.bps;
     g.epr = E / g.n_dst;
+    g.dE = FastDiv(uint32_t(g.E));
+    g.dbps = FastDiv(uint32_t(std::max(g.bps, 1)));
+    g.depr = FastDiv(uint32_t(std::max(g.epr, 1)));
+    g.dTs = FastDiv(uint32_t(std::max(g.Ts, 1)));
+    g.dcap = FastDiv(uint32_t(std::max<int64_t>(std::min<int64_t>(g.cap, 0x7fffffff), 1)));
+    g.rm1 = (g.n_src > 1 || g.n_dst > 1) && g.bps == 1 && g.epr <= 64 &&
+            int64_t(g.n_dst) * (g.n_src + 1) <= 16384;   // its chunk table fits 64 KiB of LDS
     return g;
 }
 
-// Workspace: [0,256) status flag; blk_flags [B]; blk_counts [B][E]; blk_base [B][E].
-// The flag is overwritten (never accumulated across calls), so nothing needs clearing.
-size_t ws_bytes_for(const PlanGeom &g) {
-    return 256 + align256(size_t(g.B) * sizeof(int)) + 2 * align256(size_t(g.B) * g.E * sizeof(int));
+// Workspace: [0,256) status flag; blk_flags [B]; blk_counts [B][E]; blk_base [B][E];
+// rank [T*k] bytes. The flag is overwritten (never accumulated across calls) and every
+// other entry a call reads it has written first, so nothing needs clearing.
+// With the one-block-per-source path also: within [B][E] (rows before expert e inside
+// its destination chunk) and csize [B][n_dst] (rows the source sends to each
+// destination).
+struct WsLayout {
+    size_t flags, counts, base, rank, within, csize, total;
+};
+WsLayout ws_layout(const PlanGeom &g) {
+    WsLayout l;
+    l.flags = 256;
+    l.counts = l.flags + align256(size_t(g.B) * sizeof(int));
+    l.base = l.counts + align256(size_t(g.B) * g.E * sizeof(int));
+    l.rank = l.base + align256(size_t(g.B) * g.E * sizeof(int));
+    l.within = l.rank + align256(size_t(g.T) * g.k);
+    l.csize = l.within + (g.rm1 ? align256(size_t(g.B) * g.E * sizeof(int)) : 0);
+    l.total = l.csize + (g.rm1 ? align256(size_t(g.B) * g.n_dst * sizeof(int)) : 0);
+    return l;
 }
+size_t ws_bytes_for(const PlanGeom &g) { return ws_layout(g).total; }
 
-__device__ __forceinline__ void build_masks(unsigned long long *masks, const int *idx,
-                                            int t_begin, int n, int k, int E, int *flag) {
-    for (int i = threadIdx.x; i < E * kMaskWords; i += blockDim.x) masks[i] = 0ull;
-    __syncthreads();
-    const int t = threadIdx.x;
-    if (t < n) {
-        for (int j = 0; j < k; ++j) {
-            const int e = idx[size_t(t_begin + t) * k + j];
-            if (e < 0 || e >= E) {
-                atomicOr(flag, kFlagBadIndex);
-                continue;
-            }
-            const unsigned long long bit = 1ull << (t & 63);
-            const unsigned long long old = atomicOr(&masks[e * kMaskWords + (t >> 6)], bit);
-            if (old & bit) atomicOr(flag, kFlagBadIndex);   // expert listed twice
-        }
+constexpr int kMaxK = 32;
+
+// sum_{i < n} a[i * stride] with eight LDS loads in flight
+__device__ __forceinline__ int lds_strided_sum(const int *a, int n, int stride) {
+    int c = 0, i = 0;
+    for (; i + 8 <= n; i += 8) {
+        int w[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) w[u] = a[(i + u) * stride];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c += w[u];
     }
-    __syncthreads();
+    for (; i < n; ++i) c += a[i * stride];
+    return c;
 }
 
+
+// Counts and ranks of one plan block. Thread t loads its token's k expert ids first
+// (all loads in flight together), then sets its bits.
 __global__ __launch_bounds__(kPlanBlock) void k_plan_count(const int *__restrict__ idx, PlanGeom g,
                                                           int *__restrict__ blk_counts,
-                                                          int *__restrict__ blk_flags) {
+                                                          int *__restrict__ blk_flags,
+                                                          unsigned char *__restrict__ rank,
+                                                          int *__restrict__ within,
+                                                          int *__restrict__ csize) {
     extern __shared__ unsigned long long masks[];
+    int *cnt_l = reinterpret_cast<int *>(masks + g.E * kMaskWords);   // [E], rm1 only
     __shared__ int bflag;
     const int b = blockIdx.x;
     const int s = b / g.bps, tb = (b % g.bps) * kPlanBlock;
     const int n = min(kPlanBlock, g.Ts - tb);
-    if (threadIdx.x == 0) bflag = 0;
-    build_masks(masks, idx, s * g.Ts + tb, n, g.k, g.E, &bflag);
-    if (threadIdx.x == 0) blk_flags[b] = bflag;
-    for (int e = threadIdx.x; e < g.E; e += blockDim.x) {
+    const int t = threadIdx.x;
+    const size_t p0 = size_t(s * g.Ts + tb + t) * g.k;      // this token's first pair
+    int ev[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) ev[j] = (j < g.k && t < n) ? idx[p0 + j] : -1;
+    if (t == 0) bflag = 0;
+    for (int i = t; i < g.E * kMaskWords; i += blockDim.x) masks[i] = 0ull;
+    __syncthreads();
+    const unsigned long long bit = 1ull << (t & 63);
+    if (t < n) {
+        int fl = 0;
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
+            if (j >= g.k) break;
+            const int e = ev[j];
+            if (e < 0 || e >= g.E) {
+                fl = kFlagBadIndex;
+                continue;
+            }
+            const unsigned long long old = atomicOr(&masks[e * kMaskWords + (t >> 6)], bit);
+            if (old & bit) fl = kFlagBadIndex;              // expert listed twice
+        }
+        if (fl) atomicOr(&bflag, fl);
+    }
+    __syncthreads();
+    if (t == 0) blk_flags[b] = bflag;
+    for (int e = t; e < g.E; e += blockDim.x) {
         int c = 0;
 #pragma unroll
         for (int w = 0; w < kMaskWords; ++w) c += __popcll(masks[e * kMaskWords + w]);
         blk_counts[size_t(b) * g.E + e] = c;
+        if (g.rm1) cnt_l[e] = c;
+    }
+    if (g.rm1) {
+        __syncthreads();
+        // this source's rows before expert e inside its chunk for e's destination, and
+        // its chunk size per destination (at most 64 experts per destination)
+        for (int e = t; e < g.E; e += blockDim.x) {
+            const int r0 = g.depr.div(e) * g.epr;
+            within[size_t(b) * g.E + e] = lds_strided_sum(cnt_l + r0, e - r0, 1);
+        }
+        for (int r = t; r < g.n_dst; r += blockDim.x)
+            csize[size_t(b) * g.n_dst + r] = lds_strided_sum(cnt_l + r * g.epr, g.epr, 1);
+    }
+    if (t < n) {
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
+            if (j >= g.k) break;
+            const int e = ev[j];
+            int r = 0;
+            if (e >= 0 && e < g.E) {
+                const unsigned long long *m = masks + e * kMaskWords;
+                for (int w = 0; w < (t >> 6); ++w) r += __popcll(m[w]);
+                r += __popcll(m[t >> 6] & (bit - 1ull));
+            }
+            rank[p0 + j] = static_cast<unsigned char>(r);
+        }
     }
 }
 
@@ -170,6 +251,7 @@ __device__ void seg_exclusive_scan(int *a, int n, int L, int *seg_total, int *wf
     }
 }
 
+
 // One workgroup, everything in LDS:
 //   bct [ns][E][bps]  block counts, then their prefix over the source's blocks
 //   cnt [ns][E]       per-source counts, then rows before e inside its chunk
@@ -194,18 +276,23 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_scan(
     for (int b = tid; b < g.B; b += kScanThreads)
         if (blk_flags[b]) atomicOr(&sflag, blk_flags[b]);
     // block counts, transposed so that one (source, expert)'s blocks are contiguous;
-    // thread e handles expert e (E <= kScanThreads), eight blocks' loads in flight
-    if (tid < E) {
-        for (int b0 = 0; b0 < g.B; b0 += 8) {
-            int v[8];
+    // every thread loads 16 consecutive-in-memory counts per round, all in flight
+    {
+        const int n = g.B * E;
+        for (int c0 = 0; c0 < n; c0 += 16 * kScanThreads) {
+            int v[16];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = (b0 + u < g.B) ? blk_counts[size_t(b0 + u) * E + tid] : 0;
+            for (int u = 0; u < 16; ++u) {
+                const int c = c0 + u * kScanThreads + tid;
+                v[u] = c < n ? blk_counts[c] : 0;
+            }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int b = b0 + u;
-                if (b < g.B) {
-                    const int s = b / bps, bb = b - s * bps;
-                    bct[(s * E + tid) * bps + bb] = v[u];
+            for (int u = 0; u < 16; ++u) {
+                const int c = c0 + u * kScanThreads + tid;
+                if (c < n) {
+                    const int b = g.dE.div(c), e = c - b * E;
+                    const int s = g.dbps.div(b), bb = b - s * bps;
+                    bct[(s * E + e) * bps + bb] = v[u];
                 }
             }
         }
@@ -213,18 +300,13 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_scan(
     __syncthreads();
     // per-source counts, prefix over each source's blocks
     for (int se = tid; se < ns * E; se += kScanThreads) {
-        int c = 0;
-        for (int bb = 0; bb < bps; ++bb) c += bct[se * bps + bb];
+        const int c = lds_strided_sum(bct + se * bps, bps, 1);
         cnt[se] = c;
         counts[se] = c;
     }
     __syncthreads();
     seg_exclusive_scan(bct, ns * E * bps, bps, nullptr, tf, ts);
-    for (int e = tid; e < E; e += kScanThreads) {
-        int c = 0;
-        for (int s = 0; s < ns; ++s) c += cnt[s * E + e];
-        tot[e] = c;
-    }
+    for (int e = tid; e < E; e += kScanThreads) tot[e] = lds_strided_sum(cnt + e, ns, E);
     __syncthreads();
     // rows before expert e inside (source s -> its destination); chunk sizes
     seg_exclusive_scan(cnt, ns * E, epr, segt, tf, ts);
@@ -248,16 +330,101 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_scan(
     for (int e = tid; e <= E; e += kScanThreads) expert_off[e] = tot[e];
     __syncthreads();
     if (tid == 0) *flag = sflag;      // overwrites the previous call's flag
-    // first row of every (block, expert): thread e handles expert e
+    // first row of every (block, expert), all B*E of them in parallel
+    for (int c = tid; c < g.B * E; c += kScanThreads) {
+        const int b = g.dE.div(c), e = c - b * E;
+        const int s = g.dbps.div(b), bb = b - s * bps;
+        const int r = g.depr.div(e);
+        blk_base[c] = int(int64_t(r) * g.cap) + chk[r * (ns + 1) + s] + cnt[s * E + e] +
+                      bct[(s * E + e) * bps + bb];
+    }
+}
+
+// The plan's scan for the rank-major layout with one block per source (rm1): the
+// count kernel already left each source's chunk sizes csize[s][r] and the rows before
+// every expert inside its chunk, within[s][e]; this joins the sources.
+//   chunk_off[r][s] = sum_{s' < s} csize[s'][r]   (one thread per destination)
+//   expert_off      = exclusive scan of sum_s counts[s][e]
+//   blk_base[s][e]  = r * cap + chunk_off[r][s] + within[s][e]
+__global__ __launch_bounds__(kScanThreads) void k_plan_scan_rm1(
+    const int *__restrict__ blk_counts, const int *__restrict__ blk_flags,
+    const int *__restrict__ within, const int *__restrict__ csize, PlanGeom g,
+    int *__restrict__ counts, int *__restrict__ expert_off, int *__restrict__ chunk_off,
+    int *__restrict__ blk_base, int *__restrict__ flag) {
+    extern __shared__ int chk[];                // [nd][ns + 1]
+    __shared__ int wsum[kScanThreads / kWave];
+    __shared__ int sflag;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int E = g.E, ns = g.n_src, nd = g.n_dst;
+    if (tid == 0) sflag = 0;
+    __syncthreads();
+    int fl = 0;
+    for (int b = tid; b < ns; b += kScanThreads) fl |= blk_flags[b];
+    if (fl) atomicOr(&sflag, fl);
+    // chunk offsets: destination r's senders in order, eight loads in flight
+    for (int r = tid; r < nd; r += kScanThreads) {
+        int run = 0, s = 0;
+        for (; s + 8 <= ns; s += 8) {
+            int w[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) w[u] = csize[size_t(s + u) * nd + r];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                chk[r * (ns + 1) + s + u] = run;
+                run += w[u];
+            }
+        }
+        for (; s < ns; ++s) {
+            const int w = csize[size_t(s) * nd + r];
+            chk[r * (ns + 1) + s] = run;
+            run += w;
+        }
+        chk[r * (ns + 1) + ns] = run;
+        if (int64_t(run) > g.cap) atomicOr(&sflag, kFlagCapacity);
+    }
+    // per-expert totals over the sources (and the per-source counts, which are the
+    // block counts here), eight loads in flight
+    int tot = 0;
     if (tid < E) {
-        const int r = tid / epr;
-        const int rbase = int(int64_t(r) * g.cap);
-        for (int b = 0; b < g.B; ++b) {
-            const int s = b / bps, bb = b - s * bps;
-            blk_base[size_t(b) * E + tid] = rbase + chk[r * (ns + 1) + s] + cnt[s * E + tid] +
-                                            bct[(s * E + tid) * bps + bb];
+        int s = 0;
+        for (; s + 8 <= ns; s += 8) {
+            int w[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) w[u] = blk_counts[size_t(s + u) * E + tid];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                counts[size_t(s + u) * E + tid] = w[u];
+                tot += w[u];
+            }
+        }
+        for (; s < ns; ++s) {
+            const int w = blk_counts[size_t(s) * E + tid];
+            counts[size_t(s) * E + tid] = w;
+            tot += w;
         }
     }
+    // exclusive scan of the totals over e = tid (E <= kScanThreads)
+    int v = tot;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(v, off, kWave);
+        if (lane >= off) v += o;
+    }
+    if (lane == kWave - 1) wsum[wave] = v;
+    __syncthreads();
+    int carry = 0;
+    for (int w = 0; w < wave; ++w) carry += wsum[w];
+    if (tid < E) expert_off[tid] = carry + v - tot;
+    if (tid == E - 1) expert_off[E] = carry + v;
+    for (int i = tid; i < nd * (ns + 1); i += kScanThreads) chunk_off[i] = chk[i];
+    // first row of every (source, expert)
+    for (int c = tid; c < ns * E; c += kScanThreads) {
+        const int s = g.dE.div(c), e = c - s * E;
+        const int r = g.depr.div(e);
+        blk_base[c] = int(int64_t(r) * g.cap) + chk[r * (ns + 1) + s] + within[c];
+    }
+    __syncthreads();
+    if (tid == 0) *flag = sflag;      // overwrites the previous call's flag
 }
 
 // The plan's scan for the expert-major layout (one source, one destination): thread
@@ -278,9 +445,15 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_scan_em(
     int fl = 0;
     for (int b = tid; b < g.B; b += kScanThreads) fl |= blk_flags[b];
     if (fl) atomicOr(&sflag, fl);
+    // the first kBatch blocks' counts stay in registers for the second pass
     int tot = 0;
+    int c0v[kBatch];
     if (tid < E) {
-        for (int b0 = 0; b0 < g.B; b0 += kBatch) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) c0v[u] = (u < g.B) ? blk_counts[size_t(u) * E + tid] : 0;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) tot += c0v[u];
+        for (int b0 = kBatch; b0 < g.B; b0 += kBatch) {
             int c[kBatch];
 #pragma unroll
             for (int u = 0; u < kBatch; ++u)
@@ -305,7 +478,12 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_scan_em(
     if (tid < E) {
         expert_off[tid] = off_e;
         int run = off_e;
-        for (int b0 = 0; b0 < g.B; b0 += kBatch) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            if (u < g.B) blk_base[size_t(u) * E + tid] = run;
+            run += c0v[u];
+        }
+        for (int b0 = kBatch; b0 < g.B; b0 += kBatch) {
             int c[kBatch];
 #pragma unroll
             for (int u = 0; u < kBatch; ++u)
@@ -327,14 +505,7 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_scan_em(
     if (tid == 0) *flag = sflag;      // overwrites the previous call's flag
 }
 
-// Slots, unused-row marking and the copy, fused. Workgroup (b, q) rebuilds the masks
-// of plan block b, assigns the slots of its kSubTokens tokens (pair_slot, row_pair),
-// then copies those tokens: one wavefront per token reads the row once with 16-byte
-// loads and writes it to each of its k rows. All workgroups together also mark the
-// rows no pair uses with row_pair = -1.
-constexpr int kSubTokens = 16;
-constexpr int kSubPerBlock = kPlanBlock / kSubTokens;
-
+// Slots, unused-row marking and the copy, fused: one wavefront per token.
 // Block-scaled fp8 payload of 16 consecutive elements (two 16-byte chunks of bf16) of
 // a row, for 8-lane groups that each hold one 128-element block: m = the block's
 // largest magnitude (an 8-lane max), scale = m / 448, codes = E4M3(x * (448 / m))
@@ -366,122 +537,111 @@ __device__ __forceinline__ uint4 quant16_fp8(const uint4 &v0, const uint4 &v1, f
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-constexpr int kCopyThreads = 1024;   // 16 wavefronts share a sub-block's row copies
+constexpr int kCopyThreads = 256;   // four wavefronts, one token each
 
+// Wavefront (block, wave) takes token blockIdx.x * 4 + wave: lane j < k finds the row
+// of pair j (the first row of its block and expert plus its rank inside the block),
+// records it in pair_slot and row_pair, and the wavefront then copies the row (or its
+// fp8 payload) to the k rows. All workgroups together mark the rows that no pair uses
+// with row_pair = -1.
 template <bool Q8>
-__global__ __launch_bounds__(kCopyThreads) void k_plan_slots_copy(
+__global__ __launch_bounds__(kCopyThreads) void k_plan_copy(
     const int *__restrict__ idx, PlanGeom g, const int *__restrict__ blk_base,
-    const int *__restrict__ chunk_off, int *__restrict__ pair_slot, int *__restrict__ row_pair,
-    int *__restrict__ flag, const uint4 *__restrict__ x, int rc, uint4 *__restrict__ x_disp,
-    uint4 *__restrict__ q_disp, float *__restrict__ q_scale) {
-    extern __shared__ unsigned long long masks[];
-    __shared__ int sl[kSubTokens][32];
-    const int b = blockIdx.x / kSubPerBlock, q = blockIdx.x % kSubPerBlock;
-    const int s = b / g.bps, tb = (b % g.bps) * kPlanBlock;
-    const int n = min(kPlanBlock, g.Ts - tb);
-    const int t_begin = s * g.Ts + tb;
+    const unsigned char *__restrict__ rank, const int *__restrict__ chunk_off,
+    int *__restrict__ pair_slot, int *__restrict__ row_pair, int *__restrict__ flag,
+    const uint4 *__restrict__ x, int rc, uint4 *__restrict__ x_disp, uint4 *__restrict__ q_disp,
+    float *__restrict__ q_scale) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int t = blockIdx.x * (kCopyThreads / kWave) + wave;
     const int64_t rows_total = int64_t(g.n_dst) * g.cap;
-    build_masks(masks, idx, t_begin, n, g.k, g.E, flag);   // every workgroup of block b
-    const int t = threadIdx.x;
-    if (t >= q * kSubTokens && t < (q + 1) * kSubTokens && t < n) {
-        const int tg = t_begin + t;
-        for (int j = 0; j < g.k; ++j) {
-            const int e = idx[size_t(tg) * g.k + j];
-            int slot = -1;
-            if (e >= 0 && e < g.E) {
-                const unsigned long long *m = masks + e * kMaskWords;
-                int rank = 0;
-                for (int w = 0; w < (t >> 6); ++w) rank += __popcll(m[w]);
-                rank += __popcll(m[t >> 6] & ((1ull << (t & 63)) - 1ull));
-                const int row = blk_base[size_t(b) * g.E + e] + rank;
-                const int r = e / g.epr;
-                if (int64_t(row) - int64_t(r) * g.cap < g.cap) {
-                    slot = row;
-                    row_pair[row] = tg * g.k + j;
-                } else {
-                    atomicOr(flag, kFlagCapacity);
-                }
-            }
-            pair_slot[size_t(tg) * g.k + j] = slot;
-            sl[t - q * kSubTokens][j] = slot;
-        }
-    }
     // rows that no pair uses
     for (int64_t row = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; row < rows_total;
          row += int64_t(gridDim.x) * blockDim.x) {
-        const int r = int(row / g.cap);
+        const int r = g.dcap.div(int(row));            // row < n_dst * cap < 2^31
         if (row - int64_t(r) * g.cap >= chunk_off[r * (g.n_src + 1) + g.n_src]) row_pair[row] = -1;
     }
-    if (x == nullptr) return;
-    __syncthreads();
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int tcount = min(kSubTokens, n - q * kSubTokens);
+    if (t >= g.T) return;
+    const int s = g.dTs.div(t);
+    const int b = s * g.bps + (t - s * g.Ts) / kPlanBlock;
+    // the token's row (plain copy) is loaded before its slots are known
+    const uint4 *src = x ? x + size_t(t) * rc : nullptr;
+    int my_slot = -1;
+    if (lane < g.k) {
+        const size_t p = size_t(t) * g.k + lane;
+        const int e = idx[p];
+        if (e >= 0 && e < g.E) {
+            const int row = blk_base[size_t(b) * g.E + e] + int(rank[p]);
+            const int r = g.depr.div(e);
+            if (int64_t(row) - int64_t(r) * g.cap < g.cap) {
+                my_slot = row;
+                row_pair[row] = int(p);
+            } else {
+                atomicOr(flag, kFlagCapacity);
+            }
+        }
+        pair_slot[p] = my_slot;
+    }
+    if (src == nullptr) return;
     if (Q8) {
         // a row is rc/2 pieces of 16 elements (16 code bytes); 8 lanes hold one block.
         // Batches of 8 pieces per lane (8192 elements): all their loads in flight
         // together, then the codes; the batch's 64 block scales are gathered so that
         // lane L holds block L's, and each destination row gets them in one write.
         const int rp = rc / 2, nb = rc / 16;
-        for (int i = wave; i < tcount; i += kCopyThreads / kWave) {
-            const uint4 *src = x + size_t(t_begin + q * kSubTokens + i) * rc;
-            for (int c0 = 0; c0 < rp; c0 += 8 * kWave) {
-                uint4 v[8][2];
+        for (int c0 = 0; c0 < rp; c0 += 8 * kWave) {
+            uint4 v[8][2];
+#pragma unroll
+            for (int it = 0; it < 8; ++it) {
+                const int c = c0 + it * kWave + lane;
+                v[it][0] = make_uint4(0u, 0u, 0u, 0u);
+                v[it][1] = make_uint4(0u, 0u, 0u, 0u);
+                if (c < rp) {
+                    v[it][0] = src[2 * c];
+                    v[it][1] = src[2 * c + 1];
+                }
+            }
+            uint4 code[8];
+            float my_sc = 0.0f;
+#pragma unroll
+            for (int it = 0; it < 8; ++it) {
+                float sc;
+                code[it] = quant16_fp8(v[it][0], v[it][1], sc);   // every lane takes part
+                // block it*8 + (lane & 7) of the batch sits in lanes 8 (lane & 7) + 0..7
+                const float bs = __shfl(sc, (lane & 7) * 8, kWave);
+                if ((lane >> 3) == it) my_sc = bs;
+            }
+            const int blk = c0 / 8 + lane;                         // block held by this lane
+            for (int j = 0; j < g.k; ++j) {
+                const int sj = __builtin_amdgcn_readlane(my_slot, j);
+                if (sj < 0 || sj >= rows_total) continue;
 #pragma unroll
                 for (int it = 0; it < 8; ++it) {
                     const int c = c0 + it * kWave + lane;
-                    v[it][0] = make_uint4(0u, 0u, 0u, 0u);
-                    v[it][1] = make_uint4(0u, 0u, 0u, 0u);
-                    if (c < rp) {
-                        v[it][0] = src[2 * c];
-                        v[it][1] = src[2 * c + 1];
-                    }
+                    if (c < rp) q_disp[size_t(sj) * rp + c] = code[it];
                 }
-                uint4 code[8];
-                float my_sc = 0.0f;
-#pragma unroll
-                for (int it = 0; it < 8; ++it) {
-                    float sc;
-                    code[it] = quant16_fp8(v[it][0], v[it][1], sc);   // every lane takes part
-                    // block it*8 + (lane & 7) of the batch sits in lanes 8 (lane & 7) + 0..7
-                    const float bs = __shfl(sc, (lane & 7) * 8, kWave);
-                    if ((lane >> 3) == it) my_sc = bs;
-                }
-                const int blk = c0 / 8 + lane;                         // block held by this lane
-                for (int j = 0; j < g.k; ++j) {
-                    const int sj = sl[i][j];
-                    if (sj < 0 || sj >= rows_total) continue;
-#pragma unroll
-                    for (int it = 0; it < 8; ++it) {
-                        const int c = c0 + it * kWave + lane;
-                        if (c < rp) q_disp[size_t(sj) * rp + c] = code[it];
-                    }
-                    if (blk < nb) q_scale[size_t(sj) * nb + blk] = my_sc;
-                }
+                if (blk < nb) q_scale[size_t(sj) * nb + blk] = my_sc;
             }
         }
         return;
     }
-    for (int i = wave; i < tcount; i += kCopyThreads / kWave) {
-        const uint4 *src = x + size_t(t_begin + q * kSubTokens + i) * rc;
-        // batches of 16 KiB of the row (16 pieces per lane) with all loads in flight
-        for (int c0 = 0; c0 < rc; c0 += 16 * kWave) {
-            uint4 v[16];
+    // batches of 16 KiB of the row (16 pieces per lane) with all loads in flight
+    for (int c0 = 0; c0 < rc; c0 += 16 * kWave) {
+        uint4 v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int c = c0 + u * kWave + lane;
+            v[u] = make_uint4(0u, 0u, 0u, 0u);
+            if (c < rc) v[u] = src[c];
+        }
+        for (int j = 0; j < g.k; ++j) {
+            const int sj = __builtin_amdgcn_readlane(my_slot, j);
+            if (sj < 0 || sj >= rows_total) continue;
+            uint4 *dst = x_disp + size_t(sj) * rc;
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
                 const int c = c0 + u * kWave + lane;
-                v[u] = make_uint4(0u, 0u, 0u, 0u);
-                if (c < rc) v[u] = src[c];
-            }
-            for (int j = 0; j < g.k; ++j) {
-                const int sj = sl[i][j];
-                if (sj < 0 || sj >= rows_total) continue;
-                uint4 *dst = x_disp + size_t(sj) * rc;
-#pragma unroll
-                for (int u = 0; u < 16; ++u) {
-                    const int c = c0 + u * kWave + lane;
-                    if (c < rc) dst[c] = v[u];
-                }
+                if (c < rc) dst[c] = v[u];
             }
         }
     }
@@ -673,28 +833,38 @@ moe_status_t dispatch_impl(const void *x, const int32_t *topk_idx, int64_t T, in
     if (!set_scan_lds_limit()) return MOE_ERR_HIP;   // first HIP call: all checks done
     const hipStream_t st = as_stream(stream);
     char *wsb = static_cast<char *>(ws);
+    const WsLayout wl = ws_layout(g);
     int *flag = reinterpret_cast<int *>(wsb);
-    int *blk_flags = reinterpret_cast<int *>(wsb + 256);
-    int *blk_counts = reinterpret_cast<int *>(wsb + 256 + align256(size_t(g.B) * sizeof(int)));
-    int *blk_base = blk_counts + align256(size_t(g.B) * E * sizeof(int)) / sizeof(int);
-    const size_t lds_mask = size_t(E) * kMaskWords * sizeof(unsigned long long);
+    int *blk_flags = reinterpret_cast<int *>(wsb + wl.flags);
+    int *blk_counts = reinterpret_cast<int *>(wsb + wl.counts);
+    int *blk_base = reinterpret_cast<int *>(wsb + wl.base);
+    unsigned char *rank = reinterpret_cast<unsigned char *>(wsb + wl.rank);
+    int *within = g.rm1 ? reinterpret_cast<int *>(wsb + wl.within) : nullptr;
+    int *csize = g.rm1 ? reinterpret_cast<int *>(wsb + wl.csize) : nullptr;
+    const size_t lds_mask = size_t(E) * kMaskWords * sizeof(unsigned long long) +
+                            (g.rm1 ? size_t(E) * sizeof(int) : 0);
 
     hipLaunchKernelGGL(k_plan_count, dim3(g.B), dim3(kPlanBlock), lds_mask, st, topk_idx, g,
-                       blk_counts, blk_flags);
-    if (expert_major)
+                       blk_counts, blk_flags, rank, within, csize);
+    if (g.rm1)
+        hipLaunchKernelGGL(k_plan_scan_rm1, dim3(1), dim3(kScanThreads),
+                           size_t(n_dst) * (n_src + 1) * sizeof(int), st, blk_counts, blk_flags,
+                           within, csize, g, counts, expert_off, chunk_off, blk_base, flag);
+    else if (expert_major)
         hipLaunchKernelGGL(k_plan_scan_em, dim3(1), dim3(kScanThreads), 0, st, blk_counts,
                            blk_flags, g, counts, expert_off, chunk_off, blk_base, flag);
     else
         hipLaunchKernelGGL(k_plan_scan, dim3(1), dim3(kScanThreads), lds_scan, st, blk_counts,
                            blk_flags, g, counts, expert_off, chunk_off, blk_base, flag);
+    const dim3 cgrid(unsigned(cdiv(T, kCopyThreads / kWave)));
     if (q8)
-        hipLaunchKernelGGL(k_plan_slots_copy<true>, dim3(g.B * kSubPerBlock), dim3(kCopyThreads),
-                           lds_mask, st, topk_idx, g, blk_base, chunk_off, pair_slot, row_pair, flag,
+        hipLaunchKernelGGL(k_plan_copy<true>, cgrid, dim3(kCopyThreads), 0, st, topk_idx, g,
+                           blk_base, rank, chunk_off, pair_slot, row_pair, flag,
                            static_cast<const uint4 *>(x), int(rowb / 16), nullptr,
                            reinterpret_cast<uint4 *>(q_disp), q_scale);
     else
-        hipLaunchKernelGGL(k_plan_slots_copy<false>, dim3(g.B * kSubPerBlock), dim3(kCopyThreads),
-                           lds_mask, st, topk_idx, g, blk_base, chunk_off, pair_slot, row_pair, flag,
+        hipLaunchKernelGGL(k_plan_copy<false>, cgrid, dim3(kCopyThreads), 0, st, topk_idx, g,
+                           blk_base, rank, chunk_off, pair_slot, row_pair, flag,
                            static_cast<const uint4 *>(x), int(rowb / 16), static_cast<uint4 *>(x_disp),
                            nullptr, nullptr);
     return launch_status();

@@ -13,41 +13,93 @@ namespace moe {
 namespace {
 
 constexpr int kRecvMaxPairs = 8192;      // local experts x senders held in LDS
+constexpr int kRecvThreads = 1024;
 
 // One workgroup. c[le][s] = counts[s][r*epr + le]. Local row of (le, s, i):
 // local_off[le] + sum_{s' < s} c[le][s'] + i; its region row:
 // chunk_off[r][s] + sum_{le' < le} c[le'][s] + i.
-__global__ __launch_bounds__(256) void k_ep_recv_plan(const int *__restrict__ counts,
-                                                      const int *__restrict__ chunk_off,
-                                                      int n_src, int E, int epr, int r,
-                                                      int cap, int *__restrict__ local_off,
-                                                      int *__restrict__ row_src) {
-    __shared__ int c[kRecvMaxPairs];
-    __shared__ int loff[1025];
-    const int tid = threadIdx.x;
+// LDS (dynamic): c [np] (then its prefix over s), cp [np] (prefix over le), rs [epr+1]
+// (row sums, then their exclusive prefix = local_off). Every prefix is taken with
+// independent loads in flight, never as one thread's chain of dependent LDS reads.
+__global__ __launch_bounds__(kRecvThreads) void k_ep_recv_plan(const int *__restrict__ counts,
+                                                               const int *__restrict__ chunk_off,
+                                                               int n_src, int E, int epr, int r,
+                                                               int cap, int *__restrict__ local_off,
+                                                               int *__restrict__ row_src) {
+    extern __shared__ int lds_plan[];
     const int np = epr * n_src;
+    int *c = lds_plan;
+    int *cp = c + np;
+    int *rs = cp + np;
+    __shared__ int scan_tmp[kRecvThreads];
+    const int tid = threadIdx.x;
     for (int p = tid; p < np; p += blockDim.x) {
         const int le = p / n_src, s = p % n_src;
         c[p] = counts[size_t(s) * E + size_t(r) * epr + le];
     }
     __syncthreads();
-    if (tid == 0) {
-        int run = 0;
-        for (int le = 0; le < epr; ++le) {
-            loff[le] = run;
-            for (int s = 0; s < n_src; ++s) run += c[le * n_src + s];
+    // cp[le][s] = sum_{le' < le} c[le'][s]: one thread per sender, eight loads in flight
+    for (int s = tid; s < n_src; s += blockDim.x) {
+        int run = 0, le = 0;
+        for (; le + 8 <= epr; le += 8) {
+            int w[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) w[u] = c[(le + u) * n_src + s];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                cp[(le + u) * n_src + s] = run;
+                run += w[u];
+            }
         }
-        loff[epr] = run;
+        for (; le < epr; ++le) {
+            const int w = c[le * n_src + s];
+            cp[le * n_src + s] = run;
+            run += w;
+        }
+    }
+    __syncthreads();   // every read of c above is done before it is rewritten in place
+    // row sums, and c[le][s] -> sum_{s' < s} c[le][s'] in place: one thread per expert
+    for (int le = tid; le < epr; le += blockDim.x) {
+        int *row = c + le * n_src;
+        int run = 0, s = 0;
+        for (; s + 8 <= n_src; s += 8) {
+            int w[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) w[u] = row[s + u];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                row[s + u] = run;
+                run += w[u];
+            }
+        }
+        for (; s < n_src; ++s) {
+            const int w = row[s];
+            row[s] = run;
+            run += w;
+        }
+        rs[le] = run;
     }
     __syncthreads();
-    for (int le = tid; le <= epr; le += blockDim.x) local_off[le] = loff[le];
+    // local_off = exclusive prefix of the row sums (epr <= 1024: one per thread)
+    int v = tid < epr ? rs[tid] : 0;
+    const int mine = v;
+    for (int off = 1; off < kRecvThreads; off <<= 1) {
+        scan_tmp[tid] = v;
+        __syncthreads();
+        if (tid >= off) v += scan_tmp[tid - off];
+        __syncthreads();
+    }
+    if (tid < epr) rs[tid] = v - mine;
+    if (tid == kRecvThreads - 1) rs[epr] = v;        // inclusive total
+    __syncthreads();
+    const int live = rs[epr];
+    for (int le = tid; le <= epr; le += blockDim.x) local_off[le] = rs[le];
     for (int p = tid; p < np; p += blockDim.x) {
         const int le = p / n_src, s = p % n_src;
-        int reg = chunk_off[size_t(r) * (n_src + 1) + s];
-        for (int l2 = 0; l2 < le; ++l2) reg += c[l2 * n_src + s];
-        int loc = loff[le];
-        for (int s2 = 0; s2 < s; ++s2) loc += c[le * n_src + s2];
-        const int n = c[p];
+        const int reg = chunk_off[size_t(r) * (n_src + 1) + s] + cp[p];
+        const int loc = rs[le] + c[p];
+        const int end = (s + 1 < n_src) ? c[p + 1] : rs[le + 1] - rs[le];
+        const int n = end - c[p];
         for (int i = 0; i < n; ++i) {
             // an over-capacity plan (flagged by the dispatch) is cut at cap, never
             // written or read past it
@@ -55,7 +107,7 @@ __global__ __launch_bounds__(256) void k_ep_recv_plan(const int *__restrict__ co
             row_src[loc + i] = (reg + i < cap) ? reg + i : -1;
         }
     }
-    for (int j = loff[epr] + tid; j < cap; j += blockDim.x) row_src[j] = -1;
+    for (int j = live + tid; j < cap; j += blockDim.x) row_src[j] = -1;
 }
 
 // Row moves, one wavefront per row with 16-byte lanes. GATHER: dst[j] = src[row_src[j]];
@@ -157,8 +209,10 @@ extern "C" moe_status_t moe_ep_recv_plan(const int32_t *counts, const int32_t *c
     if (epr > 1024 || int64_t(epr) * n_src > kRecvMaxPairs || cap >= (int64_t(1) << 31))
         return MOE_ERR_UNSUPPORTED;
     if (!counts || !chunk_off || !local_off || (cap > 0 && !row_src)) return MOE_ERR_INVALID_ARG;
-    hipLaunchKernelGGL(k_ep_recv_plan, dim3(1), dim3(256), 0, as_stream(stream), counts, chunk_off,
-                       n_src, E, epr, r, int(cap), local_off, row_src);
+    const int lds = (2 * epr * n_src + epr + 1) * int(sizeof(int));
+    if (!lds_limit_once<&k_ep_recv_plan>(2 * kRecvMaxPairs * 4 + 1025 * 4)) return MOE_ERR_HIP;
+    hipLaunchKernelGGL(k_ep_recv_plan, dim3(1), dim3(kRecvThreads), lds, as_stream(stream), counts,
+                       chunk_off, n_src, E, epr, r, int(cap), local_off, row_src);
     return launch_status();
 }
 

@@ -289,6 +289,10 @@ __device__ __forceinline__ void store_rows(const unsigned char *cb, const BwdArg
     };
     const int n = it.a0 + 4 * lane;
     if (KIND == G3_DW2 || KIND == G4_DW13) {
+        // the weight gradients are written once and not read again by the layer:
+        // non-temporal stores (the cache-policy nt bit) keep them from displacing the
+        // operands in the caches (measured: expert backward 1419 -> 1373 us)
+        constexpr int kStoreNT = 2;
         const int nrows = (KIND == G3_DW2) ? d : F2;
         const int ncols = (KIND == G3_DW2) ? F : d;
         const int r0 = it.b0 + trow0;
@@ -306,7 +310,7 @@ __device__ __forceinline__ void store_rows(const unsigned char *cb, const BwdArg
                 for (int rr = 0; rr < 8; ++rr)
                     if (8 * b + rr < live)
                         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, v[rr]), rs, n * 4,
-                                                               (8 * b + rr) * ncols * 4, 0);
+                                                               (8 * b + rr) * ncols * 4, kStoreNT);
             }
         }
     } else if (KIND == G2_DX) {
