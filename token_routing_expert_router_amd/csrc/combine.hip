@@ -192,18 +192,35 @@ __global__ __launch_bounds__(256) void k_combine_partial(const uint4 *__restrict
         while (dm) {
             const int r = __builtin_ctzll(dm);
             dm &= dm - 1;
+            // the pairs at r, j ascending (lanes whose destination is r)
+            const uint64_t at_r = __ballot(ok && my_r == r);
             for (int c = lane; c < rc; c += kWave) {
                 float acc[VN];
 #pragma unroll
                 for (int i = 0; i < VN; ++i) acc[i] = 0.0f;
-                for (int j = 0; j < k; ++j) {
-                    if (__shfl(my_r, j, kWave) != r) continue;
-                    const int s = __shfl(my_s, j, kWave);
-                    const float g = __shfl(my_g, j, kWave);
-                    float f[VN];
-                    Vec<DT>::unpack(y_disp[size_t(s) * rc + c], f);
+                // eight of those rows' loads in flight together, then their terms in j order
+                uint64_t pend = at_r;
+                while (pend) {
+                    uint4 v[8];
+                    int jj[8];
 #pragma unroll
-                    for (int i = 0; i < VN; ++i) acc[i] = __builtin_fmaf(g, f[i], acc[i]);
+                    for (int u = 0; u < 8; ++u) {
+                        jj[u] = pend ? __builtin_ctzll(pend) : -1;
+                        if (pend) pend &= pend - 1;
+                        v[u] = make_uint4(0u, 0u, 0u, 0u);
+                        if (jj[u] >= 0)
+                            v[u] = y_disp[size_t(__builtin_amdgcn_readlane(my_s, jj[u])) * rc + c];
+                    }
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        if (jj[u] < 0) continue;
+                        const float g = __builtin_bit_cast(
+                            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_g), jj[u]));
+                        float f[VN];
+                        Vec<DT>::unpack(v[u], f);
+#pragma unroll
+                        for (int i = 0; i < VN; ++i) acc[i] = __builtin_fmaf(g, f[i], acc[i]);
+                    }
                 }
                 partial[(size_t(r) * T + t) * rc + c] = Vec<DT>::pack(acc);
             }
