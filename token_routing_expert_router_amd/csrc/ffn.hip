@@ -5,16 +5,15 @@
 // to the grouped GEMM (Dispatch and combine). The expert form is not on the pages:
 // SwiGLU without biases, h = X W1^T, u = X W3^T, a = silu(h) * u, y = a W2^T.
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16, float32 accumulation. Workgroup tile 256 token
-// rows x 256 weight rows x 64 deep, eight wavefronts (each four alternating 32-row token sub-tiles x 64 weight
-// rows). For the gate/up GEMM the 256 weight rows are 128 rows of W1 and the same 128
-// rows of W3, so the SwiGLU epilogue pairs h and u in registers and writes a (and h, u
-// when they are saved for the backward). Tiles are double-buffered in LDS with an XOR
-// swizzle of 16-byte chunks. Rows are ragged per
-// expert: a tile map (m-tiles per expert, prefix-summed on the device) lets a
-// persistent grid walk (expert, m-tile, n-tile) work items; the walk gives each XCD
-// a contiguous run of items in every round so tiles that share A rows or weight
-// panels meet in the same L2.
+// bf16 path: v_mfma_f32_16x16x32_bf16, float32 accumulation. Workgroup tile 224 token
+// rows x 384 weight rows x 64 deep, eight wavefronts, LDS-direct buffer loads into
+// double-buffered stages with an XOR swizzle of 16-byte chunks. For the gate/up GEMM
+// the 384 weight rows are 192 rows of W1 and the same 192 rows of W3, so the SwiGLU
+// epilogue pairs h and u in registers and writes a (and h, u when they are saved for
+// the backward). Rows are ragged per expert: a tile map (m-tiles per expert,
+// prefix-summed on the device) lets a persistent grid walk (expert, n-tile, m-tile)
+// work items; the walk gives each XCD a contiguous run of items in every round so
+// tiles that share A rows or weight panels meet in the same L2.
 //
 // f32 path: a plain LDS-tiled vector-ALU kernel (float32 has no dense matrix-core
 // peak worth the complexity at the sizes it is used for).
@@ -27,21 +26,8 @@ namespace {
 
 enum { EPI_SWIGLU = 0, EPI_PLAIN = 1 };
 
-typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
-
-// Eight wavefronts, two per SIMD: wave w takes weight group w & 3 (64 weight rows)
-// and token group w >> 2, the 32-row token sub-tiles (w >> 2) + 2i. Each SIMD holds
-// one wave of each token group, so the MFMA work per SIMD is the same for any count of
-// live token rows, and its two waves' shares differ by at most one sub-tile.
+// Eight wavefronts, two per SIMD.
 constexpr int kFwdThreads = 512;
-constexpr int kLdsFwd = kLdsGemm;
-// Waves 0-3 issue every stage's direct loads (each the share of two waves) and alone
-// wait for the vector-memory counter; waves 4-7 carry the epilogue's global writes. So
-// one item's writes drain while the next item's stages load.
-constexpr int kLoaderWaves = 4;
-// The split pays where an item's writes are large next to its loads (down: 256 output
-// columns; gate/up when h and u are saved); gate/up writing a alone keeps every wave
-// loading and writing its own share (measured: the split costs it more than it saves).
 
 // silu(h) = h * sigmoid(h) with the hardware exp and reciprocal (the result is rounded
 // to bf16, far coarser than their error)
@@ -49,319 +35,253 @@ __device__ __forceinline__ float silu_fast(float h) {
     return h * __builtin_amdgcn_rcpf(1.0f + __expf(-h));
 }
 
-// Per-item state of the bf16 grouped GEMM: buffer resources of the token tile and
-// of the expert's weight panel, and per-lane byte offsets of the lane's 16-byte chunk
-// in the wave's A and B groups 0 and 1 (group j + 2 lies 16 rows further on, with the
-// same swizzle).
-struct GemmItem {
+// ---------------------------------------------------------------- wide tiles
+// Tile of 224 token rows x 384 weight rows x 64 deep on v_mfma_f32_16x16x32_bf16.
+// Every grouped GEMM here moves its stage loads between the L2 and the CUs at one
+// aggregate rate, so its time follows the bytes it loads per flop: each stage load
+// of a token row serves 384 weight rows instead of 256, and each weight row serves
+// up to 224 token rows. The eight wavefronts split the tile 2 x 4: wave w takes token
+// group w >> 2 (the 16-row sub-tiles (w >> 2) + 2i, up to seven) and weight group
+// w & 3 (six 16-row weight blocks), 42 blocks of 16 x 16 outputs, four accumulators
+// each: 168 registers per lane, which leaves room for double-buffered fragments at
+// two wavefronts per SIMD. Gate/up tiles hold 192 rows of W1 (tile rows 0..191) and
+// the same 192 rows of W3 (192..383), twelve 16-row blocks each; weight group g takes
+// W1 blocks g, g + 4, g + 8 and the matching W3 blocks, so h and u of one output sit
+// in one lane and register. Down tiles hold 384 consecutive rows of W2, 24 blocks;
+// weight group g takes blocks g, g + 4, ..., g + 20. Stages load only live token and
+// weight rows (an item's last n-tile may be partly past N).
+constexpr int WM = 224;                           // token rows per wide tile
+constexpr int WN = 384;                           // weight rows per wide tile
+constexpr int kLdsWA = WM * BK * 2;               // 28 KiB
+constexpr int kLdsWB = WN * BK * 2;               // 48 KiB
+constexpr int kLdsWide = 2 * (kLdsWA + kLdsWB);   // 152 KiB, double buffered
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct WideItem {
     __amdgpu_buffer_rsrc_t ra;   // token rows from the tile's first row on
     __amdgpu_buffer_rsrc_t rw;   // the expert's weight panel
-    uint32_t a_off[2], b_off[2];
-    int a_groups;                // of this wave's A groups, those holding live rows
+    uint32_t a_off;              // lane's byte offset in the wave's A group 0 (group j: +64 j rows)
+    uint32_t b_off[2];           // B groups 0-2 and 3-5 (group j: + 64 (j % 3) rows)
+    int a_groups;                // live A groups of this wave (0..4)
+    int b_mask;                  // live B groups of this wave (bit j)
     int64_t m0, m_end;           // token rows [m0, m_end) are live in this tile
     int n0;                      // first output column
 };
 
-// Direct global->LDS loads of one stage (a group is 8 rows x 128 bytes, one 1 KiB
-// wavefront instruction). Split: loading wave w moves A and B groups 8w..8w+7, the
-// other waves nothing; else wave w moves groups 4w..4w+3. Buffer loads rather than
-// global ones: the compiler then keeps its LDS waits exact.
-template <bool SPLIT>
-__device__ __forceinline__ void issue_stage(unsigned char *lds, int stage, int k0,
-                                            const GemmItem &it, int wave, int K) {
-    constexpr int NG = SPLIT ? 8 : 4;
-    if (SPLIT && wave >= kLoaderWaves) return;
-    unsigned char *As = lds + stage * (kLdsA + kLdsB);
-    unsigned char *Bs = As + kLdsA;
-    const uint32_t step = uint32_t(16 * K * 2);          // 16 rows
+// Direct global->LDS loads of one stage: A groups (8 rows x 128 bytes each) wave + 8j,
+// j < 4, of the 28; B groups wave + 8j, j < 6, of the 48.
+__device__ __forceinline__ void issue_wide(unsigned char *lds, int stage, int k0,
+                                           const WideItem &it, int wave, int K) {
+    unsigned char *As = lds + stage * (kLdsWA + kLdsWB);
+    unsigned char *Bs = As + kLdsWA;
+    const uint32_t step = uint32_t(64 * K * 2);          // 64 rows
 #pragma unroll
-    for (int j = 0; j < NG; ++j) {
+    for (int j = 0; j < 4; ++j)
         if (j < it.a_groups)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                it.ra, (__attribute__((address_space(3))) void *)(As + (wave * NG + j) * 1024), 16,
-                it.a_off[j & 1] + uint32_t(j >> 1) * step, k0 * 2, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            it.rw, (__attribute__((address_space(3))) void *)(Bs + (wave * NG + j) * 1024), 16,
-            it.b_off[j & 1] + uint32_t(j >> 1) * step, k0 * 2, 0, 0);
-    }
+                it.ra, (__attribute__((address_space(3))) void *)(As + (wave + 8 * j) * 1024), 16,
+                it.a_off + uint32_t(j) * step, k0 * 2, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 6; ++j)
+        if ((it.b_mask >> j) & 1)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                it.rw, (__attribute__((address_space(3))) void *)(Bs + (wave + 8 * j) * 1024), 16,
+                it.b_off[j / 3] + uint32_t(j % 3) * step, k0 * 2, 0, 0);
 }
 
-// LDS reads of one k16 step: the wave's two weight fragments and its NW token
-// fragments (16 bytes per lane each; rows are 128 B with chunk c stored at c ^ swz(row)).
-template <int NW>
-__device__ __forceinline__ void read_frags(const unsigned char *As, const unsigned char *Bs,
-                                           int lane, int ks, const int (&brow)[2], int trow,
-                                           bf16x8 (&wf)[2], bf16x8 (&tf)[4]) {
-    const int kc = ks * 2 + (lane >> 5);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        const int r = brow[s] + (lane & 31);
-        wf[s] = *reinterpret_cast<const bf16x8 *>(Bs + r * 128 + ((kc ^ swz(r)) << 4));
-    }
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-        const int r = trow + i * 64 + (lane & 31);
-        tf[i] = *reinterpret_cast<const bf16x8 *>(As + r * 128 + ((kc ^ swz(r)) << 4));
-    }
-}
-
-// One work item, seen by one wave with NW (0..4) live 32-row token sub-tiles: the
-// whole K loop and the epilogue, branch-free in the inner loop. A wave with no live
-// rows still moves its share of every stage and joins every barrier.
-template <int EPI, int NW, bool SPLIT>
-__device__ __forceinline__ void run_item(unsigned char *lds, const GemmItem &it,
-                                         const GemmItem &next, bool has_next, int wave,
-                                         int lane, int K, int N, uint16_t *__restrict__ out,
-                                         uint16_t *__restrict__ hu_save) {
-    const int wn = wave & 3, wm = wave >> 2;
-    f32x16 acc[4][2];
-#pragma unroll
-    for (int i = 0; i < NW; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-    // B rows of this wave's two 32-row weight sub-tiles: gate/up pairs W1 rows with
-    // the same W3 rows; down takes 64 consecutive W2 rows
-    int brow[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-        brow[s] = (EPI == EPI_SWIGLU) ? s * 128 + wn * 32 : wn * 64 + s * 32;
-    // token sub-tiles alternate between the two groups (group wm takes 32-row
-    // sub-tiles wm, wm + 2, ...), so the two wavefronts of a SIMD get equal shares of
-    // a partly filled tile
-    const int trow = wm * 32;
-
-    const int KT = K / BK;
-    const bool loader = !SPLIT || wave < kLoaderWaves;
-    // stage 0 was issued before the previous item's epilogue (or before the first item)
-    if (loader) __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < KT) issue_stage<SPLIT>(lds, cur ^ 1, (kt + 1) * BK, it, wave, K);
-        if (NW > 0) {
-            const unsigned char *As = lds + cur * (kLdsA + kLdsB);
-            const unsigned char *Bs = As + kLdsA;
-            // fragments double-buffered across the four k16 steps: the LDS reads of step
-            // ks+1 are issued before the MFMAs of step ks (sched_barrier keeps that order)
-            bf16x8 wf[2][2], tf[2][4];
-#pragma unroll
-            for (int ks = 0; ks < BK / 16; ++ks) {
-                if (ks == 0) {
-                    read_frags<NW>(As, Bs, lane, 0, brow, trow, wf[0], tf[0]);
-                    __builtin_amdgcn_sched_barrier(0);   // step 0's reads issue first
-                }
-                if (ks + 1 < BK / 16)
-                    read_frags<NW>(As, Bs, lane, ks + 1, brow, trow, wf[(ks + 1) & 1], tf[(ks + 1) & 1]);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int i = 0; i < NW; ++i)
-#pragma unroll
-                    for (int s = 0; s < 2; ++s)
-                        acc[i][s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks & 1][s], tf[ks & 1][i],
-                                                                            acc[i][s], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-        if (loader) __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the next stage landed
-        __syncthreads();                 // everyone's loads landed, and cur is free
-    }
-
-    // every wave is past its last LDS read: the next item's first stage flies into buffer
-    // 0 during this item's epilogue
-    if (has_next) issue_stage<SPLIT>(lds, 0, 0, next, wave, K);
-
-    if (!SPLIT) {
-    // direct epilogue: D = W_tile * X_tile^T, so lane l holds token column m = l & 31 and, for
-    // v = 4g + q, weight row n = 8g + 4*(l >> 5) + q: four consecutive outputs of one
-    // token row, stored as one 8-byte write per (sub-tile, g)
-    const int64_t mrow0 = it.m0 + trow + (lane & 31);   // sub-tile i at mrow0 + 64 i
-    const int nl = 4 * (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-        const int64_t m = mrow0 + i * 64;
-        if (m >= it.m_end) continue;
-        if (EPI == EPI_SWIGLU) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = it.n0 + wn * 32 + 8 * g + nl;
-                if (n >= N) continue;
-                float a4[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) a4[q] = silu_fast(acc[i][0][4 * g + q]) * acc[i][1][4 * g + q];
-                uint2 pa;
-                pa.x = pack_bf16x2(a4[0], a4[1]);
-                pa.y = pack_bf16x2(a4[2], a4[3]);
-                *reinterpret_cast<uint2 *>(out + m * N + n) = pa;
-                if (hu_save) {
-                    uint2 ph, pu;
-                    ph.x = pack_bf16x2(acc[i][0][4 * g], acc[i][0][4 * g + 1]);
-                    ph.y = pack_bf16x2(acc[i][0][4 * g + 2], acc[i][0][4 * g + 3]);
-                    pu.x = pack_bf16x2(acc[i][1][4 * g], acc[i][1][4 * g + 1]);
-                    pu.y = pack_bf16x2(acc[i][1][4 * g + 2], acc[i][1][4 * g + 3]);
-                    *reinterpret_cast<uint2 *>(hu_save + m * 2 * N + n) = ph;
-                    *reinterpret_cast<uint2 *>(hu_save + m * 2 * N + N + n) = pu;
-                }
-            }
-        } else {
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int n = it.n0 + wn * 64 + s * 32 + 8 * g + nl;
-                    if (n >= N) continue;
-                    uint2 p;
-                    p.x = pack_bf16x2(acc[i][s][4 * g], acc[i][s][4 * g + 1]);
-                    p.y = pack_bf16x2(acc[i][s][4 * g + 2], acc[i][s][4 * g + 3]);
-                    *reinterpret_cast<uint2 *>(out + m * N + n) = p;
-                }
-        }
-    }
-    return;
-    }
-
-    // split: epilogue through stage buffer 1 (64 KiB), CR token rows at a time. D = W_tile *
-    // X_tile^T: lane l holds token row trow + 64i + (l & 31) and, for v = 4g + q, weight
-    // row 8g + 4 (l >> 5) + q of sub-tile s, four consecutive outputs of one token row
-    // that go to LDS as one 8-byte bf16 piece. A chunk row is RP bytes: gate/up a (128
-    // columns, 256 B), with h and u behind it when they are saved; down 256 columns
-    // (512 B). Its 16-byte piece p sits at p ^ (row & 15). Chunks are taken starting
-    // half-way through the tile.
-    const bool save = (EPI == EPI_SWIGLU) && hu_save != nullptr;
-    const int RP = (EPI == EPI_SWIGLU) ? (save ? 768 : 256) : 512;
-    const int CR = (EPI == EPI_SWIGLU) ? (save ? 64 : 256) : 128;
-    const int nch = 256 / CR;
-    unsigned char *cb = lds + (kLdsA + kLdsB);
-#pragma unroll 1
-    for (int cc = 0; cc < nch; ++cc) {
-        const int c = (cc + nch / 2) % nch;
-        const int lo = c * CR;                               // first tile row of the chunk
-#pragma unroll
-        for (int i = 0; i < NW; ++i) {
-            const int t0 = trow + 64 * i;
-            if (t0 < lo || t0 >= lo + CR) continue;
-            const int rl = t0 - lo + (lane & 31);
-            unsigned char *row = cb + rl * RP + (lane >> 5) * 8;
-            const int sw = rl & 15;
-            if (EPI == EPI_SWIGLU) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int pc = ((wn * 4 + g) ^ sw) << 4;
-                    float a4[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) a4[q] = silu_fast(acc[i][0][4 * g + q]) * acc[i][1][4 * g + q];
-                    *reinterpret_cast<uint2 *>(row + pc) =
-                        make_uint2(pack_bf16x2(a4[0], a4[1]), pack_bf16x2(a4[2], a4[3]));
-                    if (save) {
-                        *reinterpret_cast<uint2 *>(row + 256 + pc) =
-                            make_uint2(pack_bf16x2(acc[i][0][4 * g], acc[i][0][4 * g + 1]),
-                                       pack_bf16x2(acc[i][0][4 * g + 2], acc[i][0][4 * g + 3]));
-                        *reinterpret_cast<uint2 *>(row + 512 + pc) =
-                            make_uint2(pack_bf16x2(acc[i][1][4 * g], acc[i][1][4 * g + 1]),
-                                       pack_bf16x2(acc[i][1][4 * g + 2], acc[i][1][4 * g + 3]));
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int pc = ((wn * 8 + s2 * 4 + g) ^ sw) << 4;
-                        *reinterpret_cast<uint2 *>(row + pc) =
-                            make_uint2(pack_bf16x2(acc[i][s2][4 * g], acc[i][s2][4 * g + 1]),
-                                       pack_bf16x2(acc[i][s2][4 * g + 2], acc[i][s2][4 * g + 3]));
-                    }
-            }
-        }
-        __syncthreads();
-        if (!loader) {
-            // this wave's CR/4 rows of the chunk in whole 16-byte pieces: gate/up 16 lanes
-            // per 256-byte section row (4 rows per instruction), down 32 lanes per row (2
-            // rows per instruction); buffer stores from the wave's first token row (rows
-            // past the item and columns past N are skipped)
-            const int nr = CR / 4;
-            const int r0 = (wave - kLoaderWaves) * nr;
-            const int64_t m0 = it.m0 + lo + r0;
-            const int live = int(max<int64_t>(0, min<int64_t>(nr, it.m_end - m0)));
-            constexpr int LPR = (EPI == EPI_SWIGLU) ? 16 : 32;      // lanes per row
-            constexpr int RPI = 64 / LPR;                           // rows per instruction
-            const int pr = lane % LPR, rsub = lane / LPR;
-            const int n = it.n0 + 8 * pr;
-            const bool col = n < N;
-            const int ld = 2 * N;                                   // hu_save row length
-            const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
-                out + m0 * N, 0, int(int64_t(live) * N * 2), 0x00020000);
-#pragma unroll 4
-            for (int k = 0; k < nr / RPI; ++k) {
-                const int rr = k * RPI + rsub;
-                const int rowb = (r0 + rr) * RP + ((pr ^ ((r0 + rr) & 15)) << 4);
-                if (!(col && rr < live)) continue;
-                const uint4 v = *reinterpret_cast<const uint4 *>(cb + rowb);
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, v), ro, (rr * N + n) * 2, 0, 0);
-                if (save) {
-                    const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
-                        hu_save + m0 * ld, 0, int(int64_t(live) * ld * 2), 0x00020000);
-                    const uint4 h = *reinterpret_cast<const uint4 *>(cb + rowb + 256);
-                    const uint4 u = *reinterpret_cast<const uint4 *>(cb + rowb + 512);
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, h), rh, (rr * ld + n) * 2, 0, 0);
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, u), rh, (rr * ld + N + n) * 2, 0, 0);
-                }
-            }
-        }
-        __syncthreads();
-    }
-}
-
-// Work item -> per-wave load state. An expert's rows are split into equal m-tiles, so
-// the tiles that share one weight panel run at one speed and meet in L2; rows past the
-// allocation are never touched, whatever expert_off holds.
-template <int EPI, bool SPLIT>
-__device__ __forceinline__ GemmItem make_item(int item, const int *tile_off,
-                                              const int *__restrict__ expert_off, int E,
-                                              int n_tiles, const uint16_t *__restrict__ A,
-                                              const uint16_t *__restrict__ W, int K, int N,
-                                              int64_t rows_alloc, int wave, int lane) {
+template <int EPI>
+__device__ __forceinline__ WideItem make_wide_item(int item, const int *tile_off,
+                                                   const int *__restrict__ expert_off, int E,
+                                                   int n_tiles, const uint16_t *__restrict__ A,
+                                                   const uint16_t *__restrict__ W, int K, int N,
+                                                   int64_t rows_alloc, int wave, int lane) {
     const int Nw = (EPI == EPI_SWIGLU) ? 2 * N : N;              // weight rows per expert
-    // a direct load puts lane l's 16 bytes at row l/8, physical chunk l%8 of its
-    // 8-row group, so the XOR swizzle is applied on the global side
     const int lrow = lane >> 3;
     const int pchunk = lane & 7;
     const ItemCoord ic = decode_item(item, tile_off, E, n_tiles);
     const int e = ic.e;
-    GemmItem it;
+    WideItem it;
     const int64_t e_lo = min<int64_t>(expert_off[e], rows_alloc);
     const int64_t e_hi = min<int64_t>(expert_off[e + 1], rows_alloc);
     const int mc = tile_off[e + 1] - tile_off[e];
-    const int64_t rp = (e_hi - e_lo + mc - 1) / mc;     // <= BM
+    const int64_t rp = (e_hi - e_lo + mc - 1) / mc;     // <= WM
     it.m0 = e_lo + int64_t(ic.mt) * rp;
     it.m_end = min<int64_t>(e_hi, it.m0 + rp);
-    it.n0 = ic.nt * (EPI == EPI_SWIGLU ? BNW / 2 : BNW);
-    // byte ranges of the two resources (loads past them would read zeros); the host
-    // bounds the weight panel below 2^31 bytes
+    const int cols = (EPI == EPI_SWIGLU) ? WN / 2 : WN;         // output columns per tile
+    it.n0 = ic.nt * cols;
     it.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(A + it.m0 * K), 0,
-                                             int((rows_alloc - it.m0 < BM ? rows_alloc - it.m0 : BM) * K * 2),
+                                             int((rows_alloc - it.m0 < WM ? rows_alloc - it.m0 : WM) * K * 2),
                                              0x00020000);
     it.rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(W + size_t(e) * Nw * K), 0,
                                              int(size_t(Nw) * K * 2), 0x00020000);
-    const int wr0 = SPLIT ? (wave & 3) * 64 : wave * 32;        // the wave's first tile row
-    it.a_groups = int(min<int64_t>(SPLIT ? 8 : 4, max<int64_t>(0, (it.m_end - it.m0 - wr0 + 7) / 8)));
-    // Rows past the tile's data read zeros (outside the token resource) or stay inside
-    // the weight panel (gate rows past N read up rows) or past it (zeros): the outputs of
-    // such rows and columns are never stored. (Offsets of non-loading waves go unused.)
+    // tile row of the lane's row in group wave (+ 64 j): 8 wave + lrow; its swizzle
+    // depends on the row's low four bits only, the same for every j
+    const int r = 8 * wave + lrow;
+    const int c = pchunk ^ swz(r);
+    it.a_off = uint32_t((r * K + c * 8) * 2);
+    const int live = int(it.m_end - it.m0);
+    it.a_groups = 0;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int r = wr0 + j * 8 + lrow;               // tile row of group j
-        const int c = pchunk ^ swz(r);
-        it.a_off[j] = uint32_t((r * K + c * 8) * 2);
-        const int wr = (EPI == EPI_SWIGLU) ? it.n0 + (r & 127) + (r < 128 ? 0 : N) : it.n0 + r;
-        it.b_off[j] = uint32_t((size_t(wr) * K + c * 8) * 2);
+    for (int j = 0; j < 4; ++j)
+        if (wave + 8 * j < WM / 8 && 8 * (wave + 8 * j) < live) it.a_groups = j + 1;
+    const int ncol = N - it.n0;                          // output columns left (multiple of 64)
+    it.b_mask = 0;
+    if (EPI == EPI_SWIGLU) {
+        // groups 0-2: W1 rows n0 + r + 64 j; groups 3-5: W3 rows N + n0 + r + 64 (j - 3)
+        it.b_off[0] = uint32_t((size_t(it.n0 + r) * K + c * 8) * 2);
+        it.b_off[1] = uint32_t((size_t(N + it.n0 + r) * K + c * 8) * 2);
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+            if (8 * (wave + 8 * j) < ncol) it.b_mask |= 9 << j;
+    } else {
+        it.b_off[0] = uint32_t((size_t(it.n0 + r) * K + c * 8) * 2);
+        it.b_off[1] = it.b_off[0] + uint32_t(3 * 64 * K * 2);
+#pragma unroll
+        for (int j = 0; j < 6; ++j)
+            if (8 * (wave + 8 * j) < ncol) it.b_mask |= 1 << j;
     }
     return it;
 }
 
-template <int EPI, bool SPLIT>
-__global__ __launch_bounds__(kFwdThreads) void k_gemm_bf16(
+// One work item seen by one wave with NW (0..7) live 16-row token sub-tiles. FULL:
+// every weight sub-tile of the tile is live; else the wave skips the reads and MFMAs
+// of its sub-tiles past N (its 16-row weight blocks are wn, wn + 4, ..., so the live
+// ones of a partly filled tile spread evenly over the SIMDs).
+template <int EPI, int NW, bool FULL>
+__device__ __forceinline__ void run_wide_item(unsigned char *lds, const WideItem &it,
+                                              const WideItem &next, bool has_next, int wave,
+                                              int lane, int K, int N,
+                                              uint16_t *__restrict__ out,
+                                              uint16_t *__restrict__ hu_save) {
+    const int wn = wave & 3, wm = wave >> 2;
+    // live weight blocks of this wave: block wn + 4j is live while it starts before N
+    constexpr int J = (EPI == EPI_SWIGLU) ? 3 : 6;
+    const int nb = min(J * 4, (N - it.n0) / 16);
+    const int ls = FULL ? J : min(J, max(0, (nb - wn + 3) / 4));
+    auto live = [&](int s) { return FULL || (s % J) < ls; };
+    f32x4 acc[NW > 0 ? NW : 1][6];
+#pragma unroll
+    for (int i = 0; i < NW; ++i)
+#pragma unroll
+        for (int s = 0; s < 6; ++s) acc[i][s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // first tile row of each of the wave's weight sub-tiles
+    int wrow[6];
+#pragma unroll
+    for (int s = 0; s < 6; ++s)
+        wrow[s] = (EPI == EPI_SWIGLU) ? (s < 3 ? 16 * (wn + 4 * s) : WN / 2 + 16 * (wn + 4 * (s - 3)))
+                                      : 16 * (wn + 4 * s);
+    const int KT = K / BK;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < KT) issue_wide(lds, cur ^ 1, (kt + 1) * BK, it, wave, K);
+        if (NW > 0) {
+            const unsigned char *As = lds + cur * (kLdsWA + kLdsWB);
+            const unsigned char *Bs = As + kLdsWA;
+            // software pipeline over the stage's 2 x NW groups (k32 step ks, token
+            // sub-tile i): the token fragment of group g + 1 is read while group g's
+            // six MFMAs issue, and step 1's weight fragments while step 0 runs, so LDS
+            // latency hides behind the matrix cores (weight and token fragments
+            // double-buffered)
+            bf16x8 wf[2][6], tf[2];
+            auto rd_w = [&](int ks, bf16x8 (&dst)[6]) {
+                const int kc = ks * 4 + (lane >> 4);
+#pragma unroll
+                for (int s = 0; s < 6; ++s) {
+                    const int r = wrow[s] + (lane & 15);
+                    if (live(s))
+                        dst[s] = *reinterpret_cast<const bf16x8 *>(Bs + r * 128 + ((kc ^ swz(r)) << 4));
+                }
+            };
+            constexpr int NWD = NW > 0 ? NW : 1;
+            auto rd_t = [&](int g, bf16x8 &dst) {
+                const int ks = g / NWD, i = g % NWD;
+                const int kc = ks * 4 + (lane >> 4);
+                const int r = 16 * (wm + 2 * i) + (lane & 15);
+                dst = *reinterpret_cast<const bf16x8 *>(As + r * 128 + ((kc ^ swz(r)) << 4));
+            };
+            constexpr int NG = 2 * NWD;
+            rd_w(0, wf[0]);
+            rd_t(0, tf[0]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                if (g + 1 < NG) rd_t(g + 1, tf[(g + 1) & 1]);
+                if (g == 0) rd_w(1, wf[1]);
+                __builtin_amdgcn_sched_barrier(0);
+                const int ks = g / NWD, i = g % NWD;
+#pragma unroll
+                for (int s = 0; s < 6; ++s)
+                    if (live(s))
+                        acc[i][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[ks][s], tf[g & 1], acc[i][s], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the next stage landed
+        __syncthreads();                 // everyone's loads landed, and cur is free
+    }
+    // every wave is past its last LDS read: the next item's first stage flies into buffer
+    // 0 during this item's epilogue
+    if (has_next) issue_wide(lds, 0, 0, next, wave, K);
+
+    // D = W_tile * X_tile^T: lane l holds token column l & 15 of each token sub-tile and,
+    // in register q, weight row 4 (l >> 4) + q of each weight sub-tile: four consecutive
+    // outputs of one token row, stored as one 8-byte write
+    const int nl = 4 * (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const int64_t m = it.m0 + 16 * (wm + 2 * i) + (lane & 15);
+        if (m >= it.m_end) continue;
+        if (EPI == EPI_SWIGLU) {
+#pragma unroll
+            for (int s = 0; s < 3; ++s) {
+                const int n = it.n0 + 16 * (wn + 4 * s) + nl;
+                if (n >= N) continue;
+                float a4[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) a4[q] = silu_fast(acc[i][s][q]) * acc[i][s + 3][q];
+                *reinterpret_cast<uint2 *>(out + m * N + n) =
+                    make_uint2(pack_bf16x2(a4[0], a4[1]), pack_bf16x2(a4[2], a4[3]));
+                if (hu_save) {
+                    *reinterpret_cast<uint2 *>(hu_save + m * 2 * N + n) =
+                        make_uint2(pack_bf16x2(acc[i][s][0], acc[i][s][1]), pack_bf16x2(acc[i][s][2], acc[i][s][3]));
+                    *reinterpret_cast<uint2 *>(hu_save + m * 2 * N + N + n) =
+                        make_uint2(pack_bf16x2(acc[i][s + 3][0], acc[i][s + 3][1]),
+                                   pack_bf16x2(acc[i][s + 3][2], acc[i][s + 3][3]));
+                }
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < 6; ++s) {
+                const int n = it.n0 + 16 * (wn + 4 * s) + nl;
+                if (n >= N) continue;
+                *reinterpret_cast<uint2 *>(out + m * N + n) =
+                    make_uint2(pack_bf16x2(acc[i][s][0], acc[i][s][1]), pack_bf16x2(acc[i][s][2], acc[i][s][3]));
+            }
+        }
+    }
+}
+
+template <int EPI, bool FULL>
+__device__ __forceinline__ void wide_item_nw(int nw, unsigned char *lds, const WideItem &it,
+                                             const WideItem &next, bool has_next, int wave,
+                                             int lane, int K, int N, uint16_t *__restrict__ out,
+                                             uint16_t *__restrict__ hu_save) {
+    switch (nw) {
+    case 7: run_wide_item<EPI, 7, FULL>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
+    case 6: run_wide_item<EPI, 6, FULL>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
+    case 5: run_wide_item<EPI, 5, FULL>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
+    case 4: run_wide_item<EPI, 4, FULL>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
+    case 3: run_wide_item<EPI, 3, FULL>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
+    case 2: run_wide_item<EPI, 2, FULL>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
+    case 1: run_wide_item<EPI, 1, FULL>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
+    default: run_wide_item<EPI, 0, FULL>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
+    }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(kFwdThreads) void k_gemm_wide(
     const uint16_t *__restrict__ A,        // token rows [rows, K]
     const int *__restrict__ expert_off,    // [E+1]
     int E, const uint16_t *__restrict__ W, // [E, Nw, K]
@@ -369,42 +289,35 @@ __global__ __launch_bounds__(kFwdThreads) void k_gemm_bf16(
     uint16_t *__restrict__ out,            // [rows, N]
     uint16_t *__restrict__ hu_save,        // [rows, 2N] (gate/up only; may be null)
     int n_tiles) {
-    extern __shared__ __align__(16) unsigned char lds[];   // 2 stages x (A 32 KiB + B 32 KiB)
+    extern __shared__ __align__(16) unsigned char lds[];   // 2 stages x (A 28 KiB + B 48 KiB)
     __shared__ int tile_off[kMaxE + 1];
     __shared__ int map_scratch[256];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wavefront
-    build_tile_map(expert_off, E, BM, rows_alloc, tile_off, map_scratch);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    build_tile_map(expert_off, E, WM, rows_alloc, tile_off, map_scratch);
     const int total = tile_off[E] * n_tiles;
     const int G = gridDim.x;
-    // this workgroup's place in a round: XCD (blockIdx % 8) gets a contiguous run;
-    // rotating the place each round spreads large and small items evenly
     const int per = G / 8;
     const int slot = (G % 8 == 0) ? (blockIdx.x % 8) * per + blockIdx.x / 8 : blockIdx.x;
     if (slot >= total) return;
 
-    GemmItem it = make_item<EPI, SPLIT>(slot, tile_off, expert_off, E, n_tiles, A, W, K, N, rows_alloc,
-                                 wave, lane);
-    issue_stage<SPLIT>(lds, 0, 0, it, wave, K);
+    WideItem it = make_wide_item<EPI>(slot, tile_off, expert_off, E, n_tiles, A, W, K, N, rows_alloc,
+                                      wave, lane);
+    issue_wide(lds, 0, 0, it, wave, K);
     for (int base = 0; base < total; base += G) {
         const int nbase = base + G;
         const int nitem = nbase + (slot + nbase / G) % G;
         const bool has_next = nitem < total;
-        GemmItem next = it;
+        WideItem next = it;
         if (has_next)
-            next = make_item<EPI, SPLIT>(nitem, tile_off, expert_off, E, n_tiles, A, W, K, N, rows_alloc,
-                                  wave, lane);
-        // live 32-row token sub-tiles of this wave's token group
-        const int nsub = int(min<int64_t>(8, (it.m_end - it.m0 + 31) / 32));
-        const int nw = min(4, max(0, (nsub - (wave >> 2) + 1) / 2));
-        switch (nw) {
-        case 4: run_item<EPI, 4, SPLIT>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
-        case 3: run_item<EPI, 3, SPLIT>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
-        case 2: run_item<EPI, 2, SPLIT>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
-        case 1: run_item<EPI, 1, SPLIT>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
-        default: run_item<EPI, 0, SPLIT>(lds, it, next, has_next, wave, lane, K, N, out, hu_save); break;
-        }
+            next = make_wide_item<EPI>(nitem, tile_off, expert_off, E, n_tiles, A, W, K, N, rows_alloc,
+                                       wave, lane);
+        const int nsub = int(min<int64_t>(WM / 16, (it.m_end - it.m0 + 15) / 16));
+        const int nw = min(7, max(0, (nsub - (wave >> 2) + 1) / 2));
+        const bool full = N - it.n0 >= ((EPI == EPI_SWIGLU) ? WN / 2 : WN);
+        if (full) wide_item_nw<EPI, true>(nw, lds, it, next, has_next, wave, lane, K, N, out, hu_save);
+        else wide_item_nw<EPI, false>(nw, lds, it, next, has_next, wave, lane, K, N, out, hu_save);
         if (!has_next) break;
         it = next;
     }
@@ -493,9 +406,8 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float *__restrict__ A,
 }
 
 bool set_lds_limits() {
-    return lds_limit_once<&k_gemm_bf16<EPI_SWIGLU, false>>(kLdsFwd) &&
-           lds_limit_once<&k_gemm_bf16<EPI_SWIGLU, true>>(kLdsFwd) &&
-           lds_limit_once<&k_gemm_bf16<EPI_PLAIN, true>>(kLdsFwd);
+    return lds_limit_once<&k_gemm_wide<EPI_SWIGLU>>(kLdsWide) &&
+           lds_limit_once<&k_gemm_wide<EPI_PLAIN>>(kLdsWide);
 }
 
 // Workspace of the composite call: the activation a [rows, F] in dtype.
@@ -519,19 +431,13 @@ moe_status_t launch_gate_up(const void *x_disp, const int32_t *expert_off, const
                             void *act, void *hu_save, hipStream_t st) {
     if (dtype == MOE_BF16) {
         if (!set_lds_limits()) return MOE_ERR_HIP;
-        const int nt = int(cdiv(F, BNW / 2));
-        const int g = int(std::min<int64_t>((cdiv(rows, BM) + E) * nt, num_cus()));
-        // writing h and u as well: the loader/storer split
-        if (hu_save != nullptr)
-            hipLaunchKernelGGL((k_gemm_bf16<EPI_SWIGLU, true>), dim3(g), dim3(kFwdThreads), kLdsFwd, st,
-                               static_cast<const uint16_t *>(x_disp), expert_off, E,
-                               static_cast<const uint16_t *>(w13), int(d), int(F), rows,
-                               static_cast<uint16_t *>(act), static_cast<uint16_t *>(hu_save), nt);
-        else
-            hipLaunchKernelGGL((k_gemm_bf16<EPI_SWIGLU, false>), dim3(g), dim3(kFwdThreads), kLdsFwd, st,
-                               static_cast<const uint16_t *>(x_disp), expert_off, E,
-                               static_cast<const uint16_t *>(w13), int(d), int(F), rows,
-                               static_cast<uint16_t *>(act), nullptr, nt);
+        // one persistent workgroup per CU (the stages take 152 KiB of LDS)
+        const int nt = int(cdiv(F, WN / 2));
+        const int g = int(std::min<int64_t>((cdiv(rows, WM) + E) * nt, num_cus()));
+        hipLaunchKernelGGL((k_gemm_wide<EPI_SWIGLU>), dim3(g), dim3(kFwdThreads), kLdsWide, st,
+                           static_cast<const uint16_t *>(x_disp), expert_off, E,
+                           static_cast<const uint16_t *>(w13), int(d), int(F), rows,
+                           static_cast<uint16_t *>(act), static_cast<uint16_t *>(hu_save), nt);
     } else {
         const int nt = int(cdiv(F, FT));
         const int g = int(std::min<int64_t>((cdiv(rows, FT) + E) * nt, 4 * num_cus()));
@@ -548,9 +454,9 @@ moe_status_t launch_down(const void *act, const int32_t *expert_off, const void 
                          hipStream_t st) {
     if (dtype == MOE_BF16) {
         if (!set_lds_limits()) return MOE_ERR_HIP;
-        const int nt = int(cdiv(d, BNW));
-        const int g = int(std::min<int64_t>((cdiv(rows, BM) + E) * nt, num_cus()));
-        hipLaunchKernelGGL((k_gemm_bf16<EPI_PLAIN, true>), dim3(g), dim3(kFwdThreads), kLdsFwd, st,
+        const int nt = int(cdiv(d, WN));
+        const int g = int(std::min<int64_t>((cdiv(rows, WM) + E) * nt, num_cus()));
+        hipLaunchKernelGGL((k_gemm_wide<EPI_PLAIN>), dim3(g), dim3(kFwdThreads), kLdsWide, st,
                            static_cast<const uint16_t *>(act), expert_off, E,
                            static_cast<const uint16_t *>(w2), int(F), int(d), rows,
                            static_cast<uint16_t *>(y_disp), nullptr, nt);
