@@ -29,6 +29,13 @@ enum { EPI_SWIGLU = 0, EPI_PLAIN = 1 };
 // Eight wavefronts, two per SIMD.
 constexpr int kFwdThreads = 512;
 
+// Workgroup barrier after this wave's LDS operations complete, without waiting for
+// its global stores or direct loads (__syncthreads also waits for those). The memory
+// clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // silu(h) = h * sigmoid(h) with the hardware exp and reciprocal (the result is rounded
 // to bf16, far coarser than their error)
 __device__ __forceinline__ float silu_fast(float h) {
@@ -225,40 +232,59 @@ __device__ __forceinline__ void run_wide_item(unsigned char *lds, const WideItem
     // 0 during this item's epilogue
     if (has_next) issue_wide(lds, 0, 0, next, wave, K);
 
+    // Epilogue through stage buffer 1, which is idle until the next item's first barrier.
     // D = W_tile * X_tile^T: lane l holds token column l & 15 of each token sub-tile and,
-    // in register q, weight row 4 (l >> 4) + q of each weight sub-tile: four consecutive
-    // outputs of one token row, stored as one 8-byte write
+    // in register q, weight row 4 (l >> 4) + q of each weight block, so a direct store
+    // would write 32-byte pieces of 16 rows. Instead each output matrix (a, and h, u
+    // when saved; y for down) goes to LDS 96 tile rows at a time and from there to
+    // memory as whole rows, 16 bytes per lane. The barriers here wait for LDS only: the
+    // stores and the next item's first stage stay in flight.
+    constexpr int COLS = (EPI == EPI_SWIGLU) ? WN / 2 : WN;   // output columns per tile
+    constexpr int PPR = COLS / 8;                             // 16-byte pieces per row
+    constexpr int PITCH = COLS * 2 + 16;                      // LDS row pitch (bytes)
+    constexpr int CR = 96;                                    // tile rows per chunk
+    static_assert(CR * PITCH <= kLdsWA + kLdsWB, "an epilogue chunk fits one stage buffer");
+    unsigned char *cb = lds + (kLdsWA + kLdsWB);
+    const int live_rows = int(it.m_end - it.m0);
+    const int nmat = (EPI == EPI_SWIGLU && hu_save != nullptr) ? 3 : 1;
+    const int tid = int(threadIdx.x);
     const int nl = 4 * (lane >> 4);
+    // every wave runs the same chunks and barriers (its own sub-tiles may end sooner)
 #pragma unroll
-    for (int i = 0; i < NW; ++i) {
-        const int64_t m = it.m0 + 16 * (wm + 2 * i) + (lane & 15);
-        if (m >= it.m_end) continue;
-        if (EPI == EPI_SWIGLU) {
+    for (int c = 0; c < (WM + CR - 1) / CR; ++c) {            // token sub-tiles 3c..3c+2
+        if (c * CR >= live_rows) break;
 #pragma unroll
-            for (int s = 0; s < 3; ++s) {
-                const int n = it.n0 + 16 * (wn + 4 * s) + nl;
-                if (n >= N) continue;
-                float a4[4];
+        for (int o = 0; o < ((EPI == EPI_SWIGLU) ? 3 : 1); ++o) {
+            if (o >= nmat) break;
+            uint16_t *dst = o == 0 ? out : hu_save + (o == 2 ? N : 0);
+            const int64_t ld = o == 0 ? N : 2 * int64_t(N);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) a4[q] = silu_fast(acc[i][s][q]) * acc[i][s + 3][q];
-                *reinterpret_cast<uint2 *>(out + m * N + n) =
-                    make_uint2(pack_bf16x2(a4[0], a4[1]), pack_bf16x2(a4[2], a4[3]));
-                if (hu_save) {
-                    *reinterpret_cast<uint2 *>(hu_save + m * 2 * N + n) =
-                        make_uint2(pack_bf16x2(acc[i][s][0], acc[i][s][1]), pack_bf16x2(acc[i][s][2], acc[i][s][3]));
-                    *reinterpret_cast<uint2 *>(hu_save + m * 2 * N + N + n) =
-                        make_uint2(pack_bf16x2(acc[i][s + 3][0], acc[i][s + 3][1]),
-                                   pack_bf16x2(acc[i][s + 3][2], acc[i][s + 3][3]));
+            for (int i = 3 * c; i < NW && i < 3 * c + 3; ++i) {
+                unsigned char *row = cb + (16 * (wm + 2 * (i % 3)) + (lane & 15)) * PITCH + nl * 2;
+#pragma unroll
+                for (int s = 0; s < ((EPI == EPI_SWIGLU) ? 3 : 6); ++s) {
+                    if (!live(s)) continue;
+                    float v[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        if (EPI == EPI_PLAIN) v[q] = acc[i][s][q];
+                        else if (o == 0) v[q] = silu_fast(acc[i][s][q]) * acc[i][s + 3][q];
+                        else v[q] = acc[i][o == 1 ? s : s + 3][q];
+                    }
+                    *reinterpret_cast<uint2 *>(row + 32 * (wn + 4 * s)) =
+                        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
                 }
             }
-        } else {
-#pragma unroll
-            for (int s = 0; s < 6; ++s) {
-                const int n = it.n0 + 16 * (wn + 4 * s) + nl;
-                if (n >= N) continue;
-                *reinterpret_cast<uint2 *>(out + m * N + n) =
-                    make_uint2(pack_bf16x2(acc[i][s][0], acc[i][s][1]), pack_bf16x2(acc[i][s][2], acc[i][s][3]));
+            lds_barrier();
+            const int rows_c = min(CR, live_rows - c * CR);
+            uint16_t *base = dst + (it.m0 + int64_t(c) * CR) * ld + it.n0;
+            for (int p = tid; p < rows_c * PPR; p += kFwdThreads) {
+                const int r = p / PPR, cp = p - r * PPR;
+                if (it.n0 + 8 * cp < N)
+                    *reinterpret_cast<uint4 *>(base + r * ld + 8 * cp) =
+                        *reinterpret_cast<const uint4 *>(cb + r * PITCH + 16 * cp);
             }
+            lds_barrier();
         }
     }
 }
