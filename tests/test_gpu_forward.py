@@ -153,9 +153,16 @@ def test_dispatch_ep_layout_zipf_full(gpu_lib):
     y_disp[live_rows] = moe_synth.random_rows(wl, live_rows.numel(), device="cuda")
     y2 = moe.moe_combine(y_disp, out["pair_slot"], w.cuda())
     torch.cuda.synchronize()
-    sample = torch.arange(0, wl.T, 37)
-    ref_y = oracle.combine(y_disp.cpu(), ref["pair_slot"][sample.numpy()], w.numpy()[sample.numpy()])
-    assert oracle.normwise_rel_err(_np(y2[sample.cuda()]), ref_y) <= BF16_TOL
+    # every token against the oracle, on the live rows only (pair slots renumbered into
+    # a compact copy; the receive buffers hold 22.5 GB, mostly unused capacity)
+    live_np = live_rows.cpu().numpy()
+    compact = np.searchsorted(live_np, ref["pair_slot"])
+    assert np.array_equal(live_np[compact], ref["pair_slot"])
+    ref_y = oracle.combine(y_disp[live_rows].cpu(), compact, w.numpy())
+    err = oracle.normwise_rel_err(_np(y2), ref_y)
+    eerr = oracle.elementwise_rel_err(_np(y2), ref_y)
+    _say(f"  combine on all {wl.T} tokens: normwise {err:.3e}, elementwise {eerr:.3e}")
+    assert err <= BF16_TOL and eerr <= BF16_TOL
     del y_disp, out
     torch.cuda.empty_cache()
 

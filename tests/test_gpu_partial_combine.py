@@ -66,25 +66,36 @@ def test_partial_combine_zipf_full(gpu_lib):
     dests = ps // cap
     n_pairs = sum(len(set(dests[t].tolist())) for t in range(wl.T))
     _say(f"  return rows: {n_pairs} partial vs {wl.T * wl.k} per-expert")
-    sample = np.arange(0, wl.T, 29)
-    # the oracle per sampled token, on a compact copy of its k rows that keeps each
-    # row's destination: row dest*k + j of a region layout with cap' = k
-    yd_all = y_disp.cpu()
-    ref_part = np.zeros((wl.n_dst, len(sample), wl.d))
-    present = np.zeros((wl.n_dst, len(sample)), dtype=bool)
-    for i, t in enumerate(sample):
-        small = np.zeros((wl.n_dst * wl.k, wl.d), dtype=np.float32)
-        slot = np.zeros((1, wl.k), dtype=np.int64)
-        for j in range(wl.k):
-            slot[0, j] = dests[t, j] * wl.k + j
-            small[slot[0, j]] = _np(yd_all[ps[t, j]])
-        p1, pr1 = oracle.combine_partial(small, slot, w.numpy()[t:t + 1], wl.n_dst, wl.k)
-        ref_part[:, i], present[:, i] = p1[:, 0], pr1[:, 0]
-    ref_y = oracle.combine_from_partials(_bf16(ref_part), present)
-    got_part = part.view(wl.n_dst, wl.T, wl.d)[:, torch.from_numpy(sample).cuda()]
-    mask = torch.from_numpy(present).cuda()
-    err_p = oracle.normwise_rel_err(_np(got_part[mask]), ref_part[present])
-    err_y = oracle.normwise_rel_err(_np(y[torch.from_numpy(sample).cuda()]), ref_y)
+    # every token against the oracle, in chunks of C tokens: a chunk's rows go to a
+    # compact region layout whose regions each hold, packed in (token, j) order, the
+    # chunk's rows of that destination (cap' = the fullest region's count), so the
+    # oracle sees the same destinations and gates per token
+    yd_live = _np(y_disp[live].cpu())
+    live_np = live.cpu().numpy()
+    compact = np.searchsorted(live_np, ps)
+    assert np.array_equal(live_np[compact], ps)
+    got_all = part.view(wl.n_dst, wl.T, wl.d)
+    ref_rows, got_rows, ref_y = [], [], np.zeros((wl.T, wl.d))
+    C = 64
+    for t0 in range(0, wl.T, C):
+        t1 = min(wl.T, t0 + C)
+        dc = dests[t0:t1]
+        cap_c = int(np.bincount(dc.ravel(), minlength=wl.n_dst).max())
+        small = np.zeros((wl.n_dst * cap_c, wl.d), dtype=np.float32)
+        slot = np.zeros((t1 - t0, wl.k), dtype=np.int64)
+        fill = np.zeros(wl.n_dst, dtype=np.int64)
+        for t in range(t0, t1):
+            for j in range(wl.k):
+                r = dc[t - t0, j]
+                slot[t - t0, j] = r * cap_c + fill[r]
+                fill[r] += 1
+                small[slot[t - t0, j]] = yd_live[compact[t, j]]
+        p1, pr1 = oracle.combine_partial(small, slot, w.numpy()[t0:t1], wl.n_dst, cap_c)
+        ref_y[t0:t1] = oracle.combine_from_partials(_bf16(p1), pr1)
+        ref_rows.append(p1[pr1])
+        got_rows.append(_np(got_all[:, t0:t1][torch.from_numpy(pr1).cuda()]))
+    err_p = oracle.normwise_rel_err(np.concatenate(got_rows), np.concatenate(ref_rows))
+    err_y = oracle.normwise_rel_err(_np(y), ref_y)
     cost = oracle.normwise_rel_err(_np(y), _np(y_direct))
     _say(f"  partial err {err_p:.2e}, sum err {err_y:.2e}, vs direct combine {cost:.2e}")
     assert err_p <= BF16_TOL and err_y <= BF16_TOL and cost <= BF16_TOL
