@@ -76,7 +76,13 @@ struct WideItem {
 };
 
 // Direct global->LDS loads of one stage: A groups (8 rows x 128 bytes each) wave + 8j,
-// j < 4, of the 28; B groups wave + 8j, j < 6, of the 48.
+// j < 4, of the 28; B groups wave + 8j, j < 6, of the 48. Weight loads carry the
+// non-temporal cache-policy bit: a weight row serves only the m-tiles of its expert,
+// which run side by side, while the stream of other experts' weights would otherwise
+// push the token rows that each n-tile re-reads out of the caches (measured on the
+// 384-expert layer: HBM fetch per gate/up launch 25.4 -> 23.9 GB, 1.005 x the
+// algorithmic bytes; gate/up 4.62-4.86 -> 4.57-4.61 ms, down 2.53-2.59 -> 2.47-2.52 ms).
+constexpr int kWeightNT = 2;   // the nt bit of the buffer instruction's cache policy
 __device__ __forceinline__ void issue_wide(unsigned char *lds, int stage, int k0,
                                            const WideItem &it, int wave, int K) {
     unsigned char *As = lds + stage * (kLdsWA + kLdsWB);
@@ -93,7 +99,7 @@ __device__ __forceinline__ void issue_wide(unsigned char *lds, int stage, int k0
         if ((it.b_mask >> j) & 1)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 it.rw, (__attribute__((address_space(3))) void *)(Bs + (wave + 8 * j) * 1024), 16,
-                it.b_off[j / 3] + uint32_t(j % 3) * step, k0 * 2, 0, 0);
+                it.b_off[j / 3] + uint32_t(j % 3) * step, k0 * 2, 0, kWeightNT);
 }
 
 template <int EPI>
