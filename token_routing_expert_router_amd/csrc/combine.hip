@@ -181,7 +181,7 @@ __device__ __forceinline__ uint64_t wave_or64(uint64_t v) {
     return (uint64_t(hi) << 32) | lo;
 }
 
-template <int DT>
+template <int DT, bool NT>
 __global__ __launch_bounds__(256) void k_combine_partial(const uint4 *__restrict__ y_disp,
                                                          const int *__restrict__ pair_slot,
                                                          const float *__restrict__ topk_w, int T,
@@ -217,8 +217,14 @@ __global__ __launch_bounds__(256) void k_combine_partial(const uint4 *__restrict
                         jj[u] = pend ? __builtin_ctzll(pend) : -1;
                         if (pend) pend &= pend - 1;
                         v[u] = make_uint4(0u, 0u, 0u, 0u);
-                        if (jj[u] >= 0)
-                            v[u] = y_disp[size_t(__builtin_amdgcn_readlane(my_s, jj[u])) * rc + c];
+                        if (jj[u] >= 0) {
+                            const size_t o = size_t(__builtin_amdgcn_readlane(my_s, jj[u])) * rc + c;
+                            if (NT)
+                                v[u] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                                    reinterpret_cast<const u32x4 *>(y_disp) + o));
+                            else
+                                v[u] = y_disp[o];
+                        }
                     }
 #pragma unroll
                     for (int u = 0; u < 8; ++u) {
@@ -308,7 +314,8 @@ moe_status_t combine_impl(const void *y_disp, const int32_t *pair_slot, const fl
     const hipStream_t st = as_stream(stream);
     // Gathered rows that outgrow the 256 MB Infinity Cache are read non-temporally: they
     // arrive from HBM either way, and the hint keeps them from evicting lines that are
-    // still of use (measured on the 384-expert layer, 0.94 GB of rows: 222 -> 200 us).
+    // still of use (measured on the 384-expert layer, 0.94 GB of rows: 222 -> 200 us;
+    // the 32-source EP combine, 470 MB: 138 -> 104 us).
     // Smaller ones are mostly still in the cache from the kernel that wrote them, where
     // the hint slows the reads (100 MB: 22.7 -> 24.7 us).
     const bool nt = size_t(T) * k * rowb > (size_t(256) << 20);
@@ -394,14 +401,20 @@ extern "C" moe_status_t moe_combine_partial(const void *y_disp, const int32_t *p
     if (!topk_w) return MOE_ERR_INVALID_ARG;
     const int rc = int(d * elt_size(dtype) / 16);
     const hipStream_t st = as_stream(stream);
-    if (dtype == MOE_BF16)
-        hipLaunchKernelGGL(k_combine_partial<MOE_BF16>, dim3(row_grid(T)), dim3(256), 0, st,
-                           static_cast<const uint4 *>(y_disp), pair_slot, topk_w, int(T), k, rc,
-                           n_dst, int(cap), static_cast<uint4 *>(partial));
-    else
-        hipLaunchKernelGGL(k_combine_partial<MOE_F32>, dim3(row_grid(T)), dim3(256), 0, st,
-                           static_cast<const uint4 *>(y_disp), pair_slot, topk_w, int(T), k, rc,
-                           n_dst, int(cap), static_cast<uint4 *>(partial));
+    // the gathered rows' cache policy as in the combine
+    const bool nt = size_t(T) * k * rc * 16 > (size_t(256) << 20);
+#define MOE_PARTIAL_LAUNCH(DTV, NTV)                                                          \
+    hipLaunchKernelGGL((k_combine_partial<DTV, NTV>), dim3(row_grid(T)), dim3(256), 0, st,      \
+                       static_cast<const uint4 *>(y_disp), pair_slot, topk_w, int(T), k, rc,     \
+                       n_dst, int(cap), static_cast<uint4 *>(partial))
+    if (dtype == MOE_BF16) {
+        if (nt) MOE_PARTIAL_LAUNCH(MOE_BF16, true);
+        else MOE_PARTIAL_LAUNCH(MOE_BF16, false);
+    } else {
+        if (nt) MOE_PARTIAL_LAUNCH(MOE_F32, true);
+        else MOE_PARTIAL_LAUNCH(MOE_F32, false);
+    }
+#undef MOE_PARTIAL_LAUNCH
     return launch_status();
 }
 
