@@ -4,8 +4,9 @@ and of their backward (combine_bwd -> expert_ffn_bwd -> dispatch_bwd).
 The routing is given (not produced by the router), so these reach sizes and shapes the
 router's own limits keep out of the whole-layer tests: the largest expert count the
 plan and the grouped GEMM take (E = 1024), every token sent to the same k experts (a
-few experts with several 256-row tiles each, every other expert empty), one expert
-holding every row, and experts holding exactly one tile or one row past it. The plan
+few experts with several tiles each, every other expert empty), one expert holding
+every row, experts holding exactly one tile of rows or one row past it, and widths of
+exactly one n-tile or one n-tile plus 64 columns. The plan
 must match the oracle's bit for bit, the dispatched rows bitwise, the expert outputs
 and the combined tokens within the bf16 bar.
 """
@@ -34,8 +35,8 @@ def _routing(kind, T, E, k, seed=0):
         idx = (E - 1 - torch.arange(k, dtype=torch.int32)).repeat(T, 1)
     elif kind == "random":        # k distinct uniform experts per token
         idx = torch.argsort(torch.rand((T, E), generator=g), dim=1)[:, :k].to(torch.int32)
-    elif kind == "blocks":        # token t to experts (t // 256 + j) mod E: 256-row runs
-        base = torch.arange(T, dtype=torch.int64) // 256
+    elif kind in ("blocks", "blocks224"):   # token t to experts (t // R + j) mod E: R-row runs
+        base = torch.arange(T, dtype=torch.int64) // (256 if kind == "blocks" else 224)
         idx = ((base[:, None] + torch.arange(k)[None, :]) % E).to(torch.int32)
     else:
         raise ValueError(kind)
@@ -49,8 +50,13 @@ CASES = [
     ("same", 700, 128, 8, 3, 64),         # three experts with 700 rows (3 tiles), five empty
     ("reversed", 520, 192, 16, 2, 128),   # the last experts hold everything
     ("same", 1000, 256, 1, 1, 128),       # one expert, every row: a dense FFN of 4 tiles
-    ("blocks", 1024, 128, 4, 1, 64),      # experts of exactly 256 rows (one full tile)
+    ("blocks", 1024, 128, 4, 1, 64),      # experts of exactly 256 rows
     ("blocks", 1025, 128, 5, 1, 64),      # and one with 1 row
+    # the grouped GEMM's own tile edges (224 token rows; n-tiles of 192 gate/up and 384
+    # down columns)
+    ("blocks224", 896, 384, 4, 1, 192),   # experts of exactly 224 rows; one full n-tile each
+    ("blocks224", 897, 448, 5, 1, 256),   # and one of 1 row; a full n-tile plus 64 columns
+    ("same", 449, 768, 1, 1, 448),        # one expert of 449 rows (three m-tiles); two full down n-tiles
 ]
 
 
@@ -92,6 +98,7 @@ BWD_CASES = [
     ("random", 300, 64, 1024, 8, 64),     # the largest E: experts of 0-8 rows, many empty
     ("same", 700, 128, 8, 3, 64),         # 700-row experts: long weight-gradient contractions
     ("blocks", 1025, 128, 5, 1, 64),      # experts of 256 rows and one of 1 row
+    ("blocks224", 897, 448, 5, 1, 256),   # 224-row experts and one of 1 row; partial n-tiles
 ]
 
 
