@@ -565,7 +565,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU: the layer is one "
-                                   "GPU's share; multi-GPU runs are not part of this build",
+                                   "GPU's share; runs across several GPUs are not supported",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
     import torch
