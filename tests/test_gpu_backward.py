@@ -58,6 +58,9 @@ BWD_CASES = [
     dict(T=700, d=512, E=4, k=2, F=320),       # several 256-row tiles per expert
     dict(T=64, d=192, E=64, k=6, F=128),       # most experts empty or nearly so
     dict(T=150, d=128, E=16, k=10, F=64),      # k above 8: the multi-batch gathers
+    # the 384-expert layer's widths: dA contracts over 7168 (112 stages), dX has 28
+    # n-tiles, each expert's dW13 is 4096 x 7168
+    dict(T=64, d=7168, E=4, k=2, F=2048),
 ]
 
 
