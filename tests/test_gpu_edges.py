@@ -57,6 +57,9 @@ CASES = [
     ("blocks224", 896, 384, 4, 1, 192),   # experts of exactly 224 rows; one full n-tile each
     ("blocks224", 897, 448, 5, 1, 256),   # and one of 1 row; a full n-tile plus 64 columns
     ("same", 449, 768, 1, 1, 448),        # one expert of 449 rows (three m-tiles); two full down n-tiles
+    # the headline layer's widths on one expert of 2048 rows: ten m-tiles, 11 gate/up
+    # n-tiles (the last 128 columns wide) and 19 down n-tiles (the last 256 wide)
+    ("same", 2048, 7168, 1, 1, 2048),
 ]
 
 
