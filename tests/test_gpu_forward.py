@@ -122,6 +122,27 @@ def test_dispatch_parity_expert_major(gpu_lib, name, kw):
         assert oracle.normwise_rel_err(_np(y), inp["x"].numpy()) <= F32_TOL
 
 
+def test_dispatch_workspace_reused_across_sizes(gpu_lib):
+    """One plan workspace, sized by the first (largest) call, reused by smaller and then
+    larger batches again: every plan and every dispatched row still matches the oracle,
+    so nothing a call reads is left over from the one before."""
+    moe = gpu_lib
+    ws = None
+    for T in (4096, 1000, 37, 2500):
+        wl = _wl("mid_bf16", T=T, d=128)
+        _say(f"dispatch with a reused workspace {wl}")
+        inp = moe_synth.layer_inputs(wl, with_experts=False)
+        x = inp["x"].cuda()
+        idx, _, _ = moe.moe_route(x, inp["w_router"].cuda(), wl.k)
+        out = moe.moe_dispatch(x, idx, wl.E, out=None if ws is None else {"ws": ws})
+        ws = out["ws"]
+        assert moe.moe_dispatch_status(ws) == 0
+        ref = oracle.plan(idx.cpu().numpy(), wl.E)
+        _check_plan(out, ref)
+        ref_xd = torch.from_numpy(oracle.dispatch(inp["x"], ref["pair_slot"], wl.pairs)).to(torch.bfloat16)
+        assert torch.equal(out["x_disp"].cpu().view(torch.int16), ref_xd.view(torch.int16))
+
+
 def test_dispatch_ep_layout_zipf_full(gpu_lib):
     """32 source ranks x 128 tokens, d=7168, E=384, R=8, Zipf(1.2), buffers sized to
     N*T*max(R,E/N) = 49152 rows per destination."""
