@@ -143,6 +143,55 @@ def test_dispatch_workspace_reused_across_sizes(gpu_lib):
         assert torch.equal(out["x_disp"].cpu().view(torch.int16), ref_xd.view(torch.int16))
 
 
+@pytest.mark.parametrize("name,kw", [("mid_bf16", dict(T=700, d=384, E=16, k=4, F=448)),
+                                     ("tiny_f32", {})])
+def test_forward_outputs_written_whatever_they_held(gpu_lib, name, kw):
+    """Every output of route, dispatch, the two GEMMs and combine pre-filled with NaN,
+    then with zeros: bit-identical results, so every element the layer returns is
+    written by the call and nothing reads an output before writing it."""
+    moe = gpu_lib
+    wl = _wl(name, **kw)
+    _say(f"pre-filled outputs {wl}")
+    inp = moe_synth.layer_inputs(wl, device="cuda")
+    x, wr, w13, w2 = inp["x"], inp["w_router"], inp["w13"], inp["w2"]
+    T, k, E, F, d = wl.T, wl.k, wl.E, wl.F, wl.d
+    P = T * k
+    res = []
+    for fill in (float("nan"), 0.0):
+        f32 = dict(dtype=torch.float32, device="cuda")
+        idx = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
+        gates = torch.full((T, k), fill, **f32)
+        lg = torch.full((T, E), fill, **f32)
+        moe.moe_route(x, wr, k, topk_idx=idx, topk_w=gates, logits=lg)
+        plan = moe.moe_dispatch(x, idx, E, out={
+            "x_disp": torch.full((P, d), fill, dtype=x.dtype, device="cuda"),
+            "counts": torch.full((1, E), -7, dtype=torch.int32, device="cuda"),
+            "expert_off": torch.full((E + 1,), -7, dtype=torch.int32, device="cuda"),
+            "chunk_off": torch.full((1, 2), -7, dtype=torch.int32, device="cuda"),
+            "pair_slot": torch.full((T, k), -7, dtype=torch.int32, device="cuda"),
+            "row_pair": torch.full((P,), -7, dtype=torch.int32, device="cuda")})
+        act = torch.full((P, F), fill, dtype=x.dtype, device="cuda")
+        hu = torch.full((P, 2 * F), fill, dtype=x.dtype, device="cuda") if wl.dtype == "bf16" else None
+        moe.moe_expert_ffn_gate_up(plan["x_disp"], plan["expert_off"], w13, act=act, hu_save=hu)
+        y_disp = torch.full((P, d), fill, dtype=x.dtype, device="cuda")
+        moe.moe_expert_ffn_down(act, plan["expert_off"], w2, y_disp=y_disp)
+        y = torch.full((T, d), fill, dtype=x.dtype, device="cuda")
+        moe.moe_combine(y_disp, plan["pair_slot"], gates, y=y)
+        torch.cuda.synchronize()
+        outs = [idx, gates, lg, plan["x_disp"], plan["counts"], plan["expert_off"],
+                plan["chunk_off"], plan["pair_slot"], plan["row_pair"], act, y_disp, y]
+        if hu is not None:
+            outs.append(hu)
+        res.append([o.clone() for o in outs])
+    for a, b in zip(*res):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else
+                           (a.view(torch.int32) if a.dtype == torch.float32 else a),
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else
+                           (b.view(torch.int32) if b.dtype == torch.float32 else b))
+        if a.is_floating_point():
+            assert bool(torch.isfinite(a).all())
+
+
 def test_dispatch_ep_layout_zipf_full(gpu_lib):
     """32 source ranks x 128 tokens, d=7168, E=384, R=8, Zipf(1.2), buffers sized to
     N*T*max(R,E/N) = 49152 rows per destination."""
